@@ -1,0 +1,303 @@
+"""Benchmark of the fused FP8 MLA decode (libfp8mla.so) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--replicas R]
+
+A step is one fused decode call over one batch: mla_decode_fp8 on the batch-40
+workload (B=40 requests, 16 query heads sharing one 576-wide FP8 KV head,
+context U[1024, 8192], page size 1, pool 495,552 slots, per-tensor scale
+U[0.5, 2]) -- page-table resolution, FP8 row gather, in-kernel dequantisation,
+score MFMA, online softmax, P.V MFMA and the split-K combine.  Inputs are
+resident in HBM before timing.  R independent replicas (>= 1 GB together)
+are cycled call by call so reads come from HBM, not from the 256 MB
+Infinity Cache.
+
+Prints ONE JSON line: useful KV GB/s (576 B per attended token / call time),
+the roofline of the decode kernels against MI355X's 8 TB/s HBM peak, and the
+CPU oracle timed on the host on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "useful KV GB/s (% of HBM peak) + µs/call, FP8 MLA decode, batch 40, 4k ctx"
+HBM_PEAK_GBPS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "mla_decode_batch40_counters.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "fp8_paged_mla_amd", "csrc", "mla_decode.hip")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 4, 5])
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GB")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    return ap.parse_args()
+
+
+def source_digest(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(launch_units):
+    """HBM bytes per call from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    with open(COUNTERS_FILE) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_digest(KERNEL_SOURCE):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s=20.0):
+    """The float64 oracle on the host: requests of the same workload, one by
+    one, until about budget_s seconds have run (at least one request)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    args = (w.q.view(__import__("torch").int16).cpu().numpy().view(np.uint16),
+            w.pool.cpu().numpy(), w.indptr.cpu().numpy(), w.indices.cpu().numpy(),
+            w.scale, w.sm_scale)
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else None
+    tokens = 0
+    done = 0
+    t0 = time.perf_counter()
+    try:
+        if ctx:
+            ctx.__enter__()
+        for b in range(w.B):
+            oracle.mla_decode_ref(*args, requests=[b])
+            tokens += int(w.lengths[b])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(576.0 * tokens / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "float64 numpy oracle over %d of %d requests (%d tokens, %.1f s) of the same "
+                  "batch-40 workload, replica 0" % (done, w.B, tokens, dt),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_paged_mla_amd as fm
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    fm.library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    base = workloads.config(args.config, 0, device=dev)
+    pool_bytes = base.pool.numel()
+    R = args.replicas or max(4, math.ceil(1.0e9 / pool_bytes))
+    reps = [base] + [workloads.config(args.config, r, device=dev) for r in range(1, R)]
+    outs = [torch.empty((w.B, w.H, 512), dtype=torch.bfloat16, device=dev) for w in reps]
+    wss = [torch.empty(max(256, fm.mla_decode_fp8_workspace_bytes(w.B, w.H, w.total_tokens)),
+                       dtype=torch.uint8, device=dev) for w in reps]
+    useful = [w.useful_kv_bytes for w in reps]
+    stream = torch.cuda.current_stream(dev)
+
+    def call(i):
+        w = reps[i % R]
+        fm.mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale,
+                          out=outs[i % R], workspace=wss[i % R])
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize(dev)
+
+    # timed region: K calls cycling over replicas, one event pair around all
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        call(i)
+    stop.record(stream)
+    torch.cuda.synchronize(dev)
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    bytes_total = sum(useful[i % R] for i in range(args.steps))
+    value = bytes_total / (total_ms * 1e-3) / 1e9
+
+    # per-call distribution (same rotation), each call bracketed by events
+    per_call = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        call(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    per_call = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    q = np.percentile(per_call, [10, 50, 90])
+
+    mean_useful = bytes_total / args.steps
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": workloads.CONFIG_NAMES[args.config],
+            "batch": base.B,
+            "heads": base.H,
+            "kv_width": 576,
+            "kv_dtype": "fp8_e4m3fn",
+            "mean_tokens_per_call": round(sum(w.total_tokens for w in reps) / R, 1),
+            "replicas_rotated": R,
+            "rotated_footprint_GB": round(R * pool_bytes / 1e9, 3),
+        },
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "us_per_call": {"p10": round(float(q[0]), 2), "median": round(float(q[1]), 2),
+                        "p90": round(float(q[2]), 2)},
+        "wall_ms_timed_region": round(wall_ms, 3),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(mean_useful / (ms_per_step * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(mean_useful / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": read_traffic(1),
+            "kernel": "mla_split_kernel + mla_combine_kernel (one mla_decode_fp8 call)",
+            "algorithmic_bytes_per_call": int(mean_useful),
+        },
+    }
+
+    if not args.no_secondary:
+        result["secondary"] = secondary(fm, reps, outs, wss, stream, dev, args)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(base)
+    print(json.dumps(result), flush=True)
+
+
+def secondary(fm, reps, outs, wss, stream, dev, args):
+    """Warm (no rotation) decode, and the two cast kernels on one 495,552-slot pool."""
+    import torch
+    w = reps[0]
+    n = 50
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(5):
+        fm.mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale, out=outs[0],
+                          workspace=wss[0])
+    e0.record(stream)
+    for _ in range(n):
+        fm.mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale, out=outs[0],
+                          workspace=wss[0])
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    warm_us = e0.elapsed_time(e1) * 1e3 / n
+    res = {"decode_warm_us": round(warm_us, 2),
+           "decode_warm_GBps": round(w.useful_kv_bytes / (warm_us * 1e-6) / 1e9, 1)}
+    # cast paths on pools of 495,552 slots (rotating the replicas' pools)
+    pools = [r.pool for r in reps if r.pool.shape[0] == 495552]
+    if pools:
+        cast_out = torch.empty((495552, 576), dtype=torch.bfloat16, device=dev)
+        for p in pools:
+            fm.cast_pool_fp8_bf16(p, out=cast_out)
+        e0.record(stream)
+        for i in range(20):
+            fm.cast_pool_fp8_bf16(pools[i % len(pools)], out=cast_out)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        us = e0.elapsed_time(e1) * 1e3 / 20
+        moved = 495552 * 576 * 3
+        res["cast_pool_us"] = round(us, 2)
+        res["cast_pool_GBps"] = round(moved / (us * 1e-6) / 1e9, 1)
+        idx = reps[0].indices[:4096].contiguous()
+        g_out = torch.empty((4096, 576), dtype=torch.bfloat16, device=dev)
+        for p in pools:
+            fm.gather_cast_fp8_bf16(p, idx, out=g_out)
+        e0.record(stream)
+        for i in range(50):
+            fm.gather_cast_fp8_bf16(pools[i % len(pools)], idx, out=g_out)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        us = e0.elapsed_time(e1) * 1e3 / 50
+        res["gather_cast_4096_us"] = round(us, 2)
+        res["gather_cast_4096_GBps"] = round(4096 * (4 + 576 + 1152) / (us * 1e-6) / 1e9, 1)
+        allidx = reps[0].indices
+        n_all = allidx.shape[0]
+        g2 = torch.empty((n_all, 576), dtype=torch.bfloat16, device=dev)
+        e0.record(stream)
+        for i in range(20):
+            fm.gather_cast_fp8_bf16(pools[i % len(pools)], allidx, out=g2)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        us = e0.elapsed_time(e1) * 1e3 / 20
+        res["gather_cast_batch40_rows"] = int(n_all)
+        res["gather_cast_batch40_us"] = round(us, 2)
+        res["gather_cast_batch40_GBps"] = round(n_all * (4 + 576 + 1152) / (us * 1e-6) / 1e9, 1)
+        # plain device copy of the same pool (torch's copy kernel): measured HBM ceiling
+        src = pools[0]
+        dst = torch.empty_like(src)
+        big = torch.empty(src.numel() * 3 // 2, dtype=torch.uint8, device=dev)
+        dst2 = torch.empty_like(big)
+        for _ in range(3):
+            dst2.copy_(big)
+        e0.record(stream)
+        for _ in range(20):
+            dst2.copy_(big)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        us = e0.elapsed_time(e1) * 1e3 / 20
+        res["torch_copy_428MB_GBps"] = round(2 * big.numel() / (us * 1e-6) / 1e9, 1)
+        del dst
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+"""Python binding of libfp8mla.so: MLA decode over a paged FP8-E4M3FN latent KV
+cache, plus the full-pool and gather-then-cast FP8->BF16 casts, for MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libfp8mla.so``; PyTorch provides device memory and the current
+stream.  There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+
+The operations follow three public write-ups on FP8 KV caches for MLA models:
+"The KV Cache Cast Bottleneck" (the full-pool ``.to()`` cast of a
+``[495552, 1, 576]`` Float8_e4m3fn pool and the native-FP8 attention that
+replaces it), "The Gather-Then-Cast Pivot" (gathering only the active rows
+before casting) and "When a Faster Kernel Doesn't Speed Up Serving" (the
+CastFromFP8 history cast on the extend path).
+"""
+import ctypes
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+KV_WIDTH = 576
+V_WIDTH = 512
+MAX_HEADS = 256
+
+__all__ = [
+    "FP8MLAError",
+    "library",
+    "cast_pool_fp8_bf16",
+    "gather_cast_fp8_bf16",
+    "mla_decode_fp8",
+    "mla_decode_fp8_workspace_bytes",
+    "status_string",
+    "KV_WIDTH",
+    "V_WIDTH",
+]
+
+
+class FP8MLAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__("%s failed with status %d: %s" % (where, code, status_string(code)))
+
+
+_LIB = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libfp8mla.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            "libfp8mla.so is not built (%s missing); run `python -m fp8_paged_mla_amd.build`"
+            % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.cast_pool_fp8_bf16.argtypes = [vp, i64, vp, vp]
+    lib.cast_pool_fp8_bf16.restype = ctypes.c_int
+    lib.gather_cast_fp8_bf16.argtypes = [vp, i64, vp, i64, vp, vp]
+    lib.gather_cast_fp8_bf16.restype = ctypes.c_int
+    lib.mla_decode_fp8.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, f32, f32, vp, vp, sz, vp]
+    lib.mla_decode_fp8.restype = ctypes.c_int
+    lib.mla_decode_fp8_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.mla_decode_fp8_workspace_bytes.restype = sz
+    lib.fp8mla_status_string.argtypes = [ctypes.c_int]
+    lib.fp8mla_status_string.restype = ctypes.c_char_p
+    lib.fp8mla_abi_version.argtypes = []
+    lib.fp8mla_abi_version.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def status_string(code: int) -> str:
+    return library().fp8mla_status_string(int(code)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise FP8MLAError(status, where)
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _as_bytes(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError("%s must be float8_e4m3fn or uint8 (E4M3FN bytes), got %s" % (name, t.dtype))
+    return t
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _pool_rows(pool: torch.Tensor) -> torch.Tensor:
+    """Accept [num_slots, 576] or the pages' [num_slots, 1, 576] view."""
+    pool = _as_bytes(pool, "pool")
+    if pool.dim() == 3 and pool.shape[1] == 1:
+        pool = pool.view(pool.shape[0], pool.shape[2])
+    if pool.dim() != 2 or pool.shape[1] != KV_WIDTH:
+        raise ValueError("pool must be [num_slots, 576] (or [num_slots, 1, 576]), got %s"
+                         % (tuple(pool.shape),))
+    return pool
+
+
+def cast_pool_fp8_bf16(pool: torch.Tensor, out: torch.Tensor = None) -> torch.Tensor:
+    """BF16 copy of a whole FP8 pool: ``out[i, j] = bf16(e4m3fn(pool[i, j]))``."""
+    pool = _pool_rows(pool)
+    _require(pool, "pool")
+    dev = pool.device
+    if out is None:
+        out = torch.empty(pool.shape, dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev)
+    if tuple(out.shape) != tuple(pool.shape):
+        raise ValueError("out must be %s" % (tuple(pool.shape),))
+    with torch.cuda.device(dev):
+        _check(library().cast_pool_fp8_bf16(pool.data_ptr(), pool.shape[0], out.data_ptr(),
+                                            _stream_handle(dev)), "cast_pool_fp8_bf16")
+    return out
+
+
+def gather_cast_fp8_bf16(pool: torch.Tensor, indices: torch.Tensor,
+                         out: torch.Tensor = None) -> torch.Tensor:
+    """Compact BF16 rows of the slots named by ``indices``: ``out[r] = bf16(pool[indices[r]])``."""
+    pool = _pool_rows(pool)
+    _require(pool, "pool")
+    dev = pool.device
+    _require(indices, "indices", torch.int32, dev)
+    if indices.dim() != 1:
+        raise ValueError("indices must be 1-D")
+    n = indices.shape[0]
+    if out is None:
+        out = torch.empty((n, KV_WIDTH), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev)
+    if tuple(out.shape) != (n, KV_WIDTH):
+        raise ValueError("out must be [%d, 576]" % n)
+    with torch.cuda.device(dev):
+        _check(library().gather_cast_fp8_bf16(pool.data_ptr(), pool.shape[0], indices.data_ptr(), n,
+                                              out.data_ptr(), _stream_handle(dev)),
+               "gather_cast_fp8_bf16")
+    return out
+
+
+def mla_decode_fp8_workspace_bytes(batch: int, num_heads: int, total_tokens: int,
+                                   device=None) -> int:
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        return int(library().mla_decode_fp8_workspace_bytes(int(batch), int(num_heads),
+                                                            int(total_tokens)))
+
+
+def mla_decode_fp8(q: torch.Tensor, kv_pool: torch.Tensor, kv_indptr: torch.Tensor,
+                   kv_indices: torch.Tensor, scale: float, sm_scale: float,
+                   out: torch.Tensor = None, workspace: torch.Tensor = None) -> torch.Tensor:
+    """Fused MLA decode reading the FP8 pool directly.
+
+    q [B, H, 576] bf16; kv_pool [num_slots, 576] E4M3FN; kv_indptr [B+1] int32;
+    kv_indices [kv_indptr[B]] int32 slot ids; returns out [B, H, 512] bf16.
+    """
+    kv_pool = _pool_rows(kv_pool)
+    _require(q, "q", torch.bfloat16)
+    dev = q.device
+    _require(kv_pool, "kv_pool", None, dev)
+    _require(kv_indptr, "kv_indptr", torch.int32, dev)
+    _require(kv_indices, "kv_indices", torch.int32, dev)
+    if q.dim() != 3 or q.shape[2] != KV_WIDTH:
+        raise ValueError("q must be [B, H, 576], got %s" % (tuple(q.shape),))
+    B, H = q.shape[0], q.shape[1]
+    if kv_indptr.dim() != 1 or kv_indptr.shape[0] != B + 1:
+        raise ValueError("kv_indptr must be [B+1]")
+    if kv_indices.dim() != 1:
+        raise ValueError("kv_indices must be 1-D")
+    total = kv_indices.shape[0]
+    if out is None:
+        out = torch.empty((B, H, V_WIDTH), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev)
+    if tuple(out.shape) != (B, H, V_WIDTH):
+        raise ValueError("out must be [%d, %d, 512]" % (B, H))
+    lib = library()
+    with torch.cuda.device(dev):
+        need = int(lib.mla_decode_fp8_workspace_bytes(B, H, total))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        _require(workspace, "workspace", torch.uint8, dev)
+        ws_bytes = workspace.numel()
+        _check(lib.mla_decode_fp8(q.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
+                                  kv_indptr.data_ptr(), kv_indices.data_ptr(), total, B, H,
+                                  float(scale), float(sm_scale), out.data_ptr(),
+                                  workspace.data_ptr(), ws_bytes, _stream_handle(dev)),
+               "mla_decode_fp8")
+    return out

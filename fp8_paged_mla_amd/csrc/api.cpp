@@ -1,0 +1,119 @@
+// C ABI of libfp8mla.so: argument validation and dispatch.  Every check runs
+// on the host before any HIP call, so a rejected call touches no device.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <atomic>
+
+#include "../../include/fp8mla.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cus[kMaxDevices];
+
+// Compute units of the current device (cached per device), or -1 on error.
+int current_device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int cached = g_num_cus[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return -1;
+  if (dev < kMaxDevices) g_num_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int64_t kMaxSlots = (int64_t)UINT32_MAX;  // slot ids are 32-bit
+constexpr int64_t kMaxTokens = (int64_t)INT32_MAX;  // kv_indptr is int32
+
+}  // namespace
+
+extern "C" {
+
+int fp8mla_abi_version(void) { return 1; }
+
+const char* fp8mla_status_string(int status) {
+  switch (status) {
+    case FP8MLA_OK: return "ok";
+    case FP8MLA_ERR_NULL_PTR: return "a required pointer is NULL";
+    case FP8MLA_ERR_BAD_SHAPE: return "invalid size argument";
+    case FP8MLA_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
+    case FP8MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FP8MLA_ERR_BAD_SCALAR: return "scale must be finite and > 0, sm_scale finite";
+    case FP8MLA_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+int cast_pool_fp8_bf16(const uint8_t* pool, int64_t num_slots, uint16_t* out, void* stream) {
+  if (num_slots < 0 || num_slots > kMaxSlots) return FP8MLA_ERR_BAD_SHAPE;
+  if (num_slots == 0) return FP8MLA_OK;
+  if (!pool || !out) return FP8MLA_ERR_NULL_PTR;
+  if (!aligned16(pool) || !aligned16(out)) return FP8MLA_ERR_MISALIGNED;
+  const int cus = current_device_cus();
+  if (cus <= 0) return FP8MLA_ERR_HIP;
+  const hipError_t e =
+      fp8mla::launch_cast_pool(pool, num_slots, out, static_cast<hipStream_t>(stream), cus);
+  return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
+}
+
+int gather_cast_fp8_bf16(const uint8_t* pool, int64_t num_slots, const int32_t* indices,
+                         int64_t n, uint16_t* out, void* stream) {
+  if (n < 0 || n > kMaxTokens || num_slots < 0 || num_slots > kMaxSlots)
+    return FP8MLA_ERR_BAD_SHAPE;
+  if (n == 0) return FP8MLA_OK;
+  if (num_slots == 0) return FP8MLA_ERR_BAD_SHAPE;
+  if (!pool || !indices || !out) return FP8MLA_ERR_NULL_PTR;
+  if (!aligned16(pool) || !aligned16(out) || !aligned4(indices)) return FP8MLA_ERR_MISALIGNED;
+  const hipError_t e = fp8mla::launch_gather_cast(pool, num_slots, indices, n, out,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
+}
+
+size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens) {
+  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_tokens < 0 ||
+      total_tokens > kMaxTokens)
+    return 0;
+  if (total_tokens == 0) return 0;
+  const int cus = current_device_cus();
+  if (cus <= 0) return 0;
+  return fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus).workspace_bytes;
+}
+
+int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                   const int32_t* kv_indptr, const int32_t* kv_indices, int64_t total_tokens,
+                   int32_t batch, int32_t num_heads, float scale, float sm_scale, uint16_t* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_tokens < 0 ||
+      total_tokens > kMaxTokens || num_slots < 0 || num_slots > kMaxSlots)
+    return FP8MLA_ERR_BAD_SHAPE;
+  if (total_tokens > 0 && num_slots == 0) return FP8MLA_ERR_BAD_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.0f) || !isfinite(sm_scale)) return FP8MLA_ERR_BAD_SCALAR;
+  if (!q || !kv_indptr || !out) return FP8MLA_ERR_NULL_PTR;
+  if (total_tokens > 0 && (!kv_pool || !kv_indices || !workspace)) return FP8MLA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(out) || !aligned4(kv_indptr)) return FP8MLA_ERR_MISALIGNED;
+  if (total_tokens > 0 && (!aligned16(kv_pool) || !aligned4(kv_indices) || !aligned16(workspace)))
+    return FP8MLA_ERR_MISALIGNED;
+  const int cus = current_device_cus();
+  if (cus <= 0) return FP8MLA_ERR_HIP;
+  const fp8mla::DecodePlan plan = fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus);
+  if (workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
+  const hipError_t e = fp8mla::launch_mla_decode(q, kv_pool, num_slots, kv_indptr, kv_indices,
+                                                 total_tokens, batch, num_heads, scale, sm_scale,
+                                                 out, workspace, plan,
+                                                 static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
+}
+
+}  // extern "C"

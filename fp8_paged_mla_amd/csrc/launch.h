@@ -1,0 +1,39 @@
+// Internal host-side launch interface between the C ABI (api.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8mla {
+
+hipError_t launch_cast_pool(const uint8_t* pool, int64_t num_slots, uint16_t* out,
+                            hipStream_t stream, int num_cus);
+
+hipError_t launch_gather_cast(const uint8_t* pool, int64_t num_slots, const int32_t* indices,
+                              int64_t n, uint16_t* out, hipStream_t stream);
+
+// Decode schedule: equal token segments x head groups, and the split-K
+// workspace layout (partial outputs, then log2-sum-exp values).
+struct DecodePlan {
+  int32_t HG;          // head groups of 16
+  int32_t Hp;          // padded head count = 16 * HG
+  int32_t seg_len;     // tokens per segment (multiple of the 128-token tile)
+  int32_t nseg;        // number of segments
+  int32_t items;       // nseg * HG workgroups doing work
+  int32_t xcd_per;     // work items per XCD slot of the launch grid
+  int32_t grid;        // launched workgroups (>= items)
+  size_t lse_offset;   // byte offset of the lse array inside the workspace
+  size_t workspace_bytes;
+};
+
+DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_tokens, int num_cus);
+
+hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                             const int32_t* kv_indptr, const int32_t* kv_indices,
+                             int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
+                             float sm_scale, uint16_t* out, void* workspace, const DecodePlan& plan,
+                             hipStream_t stream);
+
+}  // namespace fp8mla

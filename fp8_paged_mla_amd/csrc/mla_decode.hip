@@ -1,0 +1,522 @@
+// Split-K MLA decode over a paged FP8-E4M3FN latent cache, for gfx950.
+//
+// What is computed (per request b, query head h; one KV head shared by all
+// heads; 576 = 512 latent + 64 rope as in "The KV Cache Cast Bottleneck",
+// The Context):
+//   s[t] = sm_scale * scale * <q[b,h,:576], e4m3(row_t[:576])>
+//   out[b,h,:] = scale * sum_t softmax(s)[t] * e4m3(row_t[:512])
+// Only the rows named by kv_indices are read, and they are dequantised in the
+// kernel: the fix the pages call for instead of the full-pool .to() cast.
+//
+// Work decomposition.  The concatenated token stream of all requests
+// (length N = kv_indptr[B]) is cut into equal segments; one workgroup
+// processes one segment for one group of 16 heads, walking it in tiles of
+// 128 tokens and handling request boundaries inside the tile.  For every
+// request it touches it writes either the final output (request entirely
+// inside the segment) or a partial (o normalised, log2-sum-exp) that the
+// combine kernel merges.  Segments are balanced by tokens, not by request,
+// so long and short requests cost the same per token.
+//
+// Inside a workgroup (8 waves, 16 heads):
+//  * wave w owns tokens [16w, 16w+16) of each tile for the score product
+//    S^T = K q^T (MFMA 16x16x32 bf16, M = 16 tokens, N = 16 heads,
+//    K = 576 in 18 steps).  Its lanes load those tokens' 576-byte rows with
+//    16-byte loads straight into registers, already in MFMA A-operand order
+//    (lane (t, g) holds 16 bytes at offset 64*i + 16*g of row t), two tiles
+//    ahead of use; the FP8 bytes are converted to bf16 right before the MFMA.
+//  * the same registers hold the value part (first 512 bytes) of each row;
+//    they are written once to LDS, where every wave reads the transposed
+//    operand it needs with ds_read_b64_tr_b8.
+//  * the softmax is exchanged through LDS: wave-local maxima, then bf16
+//    probabilities; all waves then share one running maximum per head.
+//  * wave w owns output columns [64w, 64w+64) of the P.V product
+//    O^T = V^T P^T (MFMA 16x16x32 bf16, M = 16 columns, N = 16 heads,
+//    K = 32 tokens), so no cross-wave reduction of O is needed.
+// KV bytes move from HBM exactly once per head group; every value byte is
+// converted once per wave that consumes it.
+#include "device_common.h"
+#include "launch.h"
+
+#include <math.h>
+
+namespace fp8mla {
+namespace {
+
+constexpr int NWAVES = 8;
+constexpr int THREADS = 64 * NWAVES;              // 512
+constexpr int TILE = 16 * NWAVES;                 // tokens per tile: 16 per wave
+constexpr int HEADS = 16;                         // heads per workgroup
+constexpr int VROW = V_WIDTH + 16;                // LDS bytes per value row (odd 16B-chunk stride)
+constexpr int VTILE_BYTES = TILE * VROW;          // 67584
+constexpr int KCHUNKS = KV_WIDTH / 64;            // 9 x 16-byte chunks per lane per row
+
+struct SplitParams {
+  const uint16_t* q;
+  const uint8_t* pool;
+  const int32_t* indptr;
+  const int32_t* indices;
+  uint16_t* out;
+  float* part_o;
+  float* part_lse;
+  uint32_t max_slot;
+  int32_t total_tokens;
+  int32_t B;
+  int32_t H;
+  int32_t HG;
+  int32_t Hp;
+  int32_t seg_len;
+  int32_t items;
+  int32_t xcd_per;
+  float score_scale;  // sm_scale * scale * log2(e): scores in the base-2 domain
+  float kv_scale;
+};
+
+struct CombineParams {
+  const int32_t* indptr;
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* out;
+  int32_t total_tokens;
+  int32_t B;
+  int32_t H;
+  int32_t Hp;
+  int32_t seg_len;
+  float kv_scale;
+};
+
+__device__ __forceinline__ float wave_max_over_groups(float x) {
+  // lanes h, h+16, h+32, h+48 hold the same head
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_over_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ int clamp_tok(int v, int n) { return v < 0 ? 0 : (v > n ? n : v); }
+
+// Byte mask over 4 consecutive tokens base..base+3: 0xFF for each token in
+// [lo, hi), 0 otherwise.
+__device__ __forceinline__ uint32_t run_mask(int base, int lo, int hi) {
+  const int a = min(max(lo - base, 0), 4);
+  const int b = min(max(hi - base, 0), 4);
+  if (b <= a) return 0u;
+  const uint64_t upto_b = (b == 4) ? 0xFFFFFFFFull : ((1ull << (8 * b)) - 1ull);
+  const uint64_t below_a = (1ull << (8 * a)) - 1ull;
+  return (uint32_t)(upto_b & ~below_a);
+}
+
+// Token row (tile-relative) held by MFMA row m of wave w.  Odd waves use
+// row m ^ 12 so that the transposed LDS reads of two consecutive waves'
+// rows fall in distinct banks.
+__device__ __forceinline__ int tile_row(int w, int m) { return 16 * w + ((w & 1) ? (m ^ 12) : m); }
+
+__global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2 * VTILE_BYTES];
+  __shared__ float mx_lds[NWAVES][HEADS];
+  __shared__ uint2 p_lds[NWAVES][64];
+  __shared__ float l_lds[NWAVES][HEADS];
+  __shared__ u32x4_t q_lds[2 * KCHUNKS][64];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = lane & 15;  // MFMA row/column index inside the 16-lane group
+  const int g = lane >> 4;  // 16-lane group
+
+  int item = blockIdx.x;
+  if (p.HG > 1) item = (int)(blockIdx.x & 7) * p.xcd_per + (int)(blockIdx.x >> 3);
+  if (item >= p.items) return;
+  const int seg = item / p.HG;
+  const int hg = item - seg * p.HG;
+  const int N = p.total_tokens;
+  const int seg_lo = seg * p.seg_len;
+  const int seg_hi = min(N, seg_lo + p.seg_len);
+  if (seg_lo >= seg_hi) return;
+  const int ntiles = (seg_hi - seg_lo + TILE - 1) / TILE;
+  const int head = hg * HEADS + t;  // head whose scores / outputs this lane carries
+
+  // ---- token rows: lane loads row krow of every tile
+  const int krow = tile_row(w, t);
+  // Loads in the pipelined loop are unconditional (a branch around them
+  // makes the compiler drain every outstanding load at the join).  A lane
+  // whose token lies past the segment reads the segment's first row instead
+  // -- a cache hit on a line another lane fetches -- and process_tile zeroes
+  // that lane's data.
+  auto load_index = [&](int k) -> int32_t {
+    const int tok = seg_lo + k * TILE + krow;
+    return p.indices[tok < seg_hi ? tok : seg_lo];
+  };
+  auto load_rows = [&](int32_t idx, u32x4_t (&kb)[KCHUNKS]) {
+    const uint32_t s = (uint32_t)idx < p.max_slot ? (uint32_t)idx : p.max_slot;
+    const uint8_t* rp = p.pool + (uint64_t)s * KV_WIDTH + 16 * g;
+#pragma unroll
+    for (int i = 0; i < KCHUNKS; ++i) kb[i] = load16_nt(rp + 64 * i);
+  };
+
+  u32x4_t kb0[KCHUNKS], kb1[KCHUNKS], kb2[KCHUNKS];
+  int32_t ix0 = load_index(0);
+  int32_t ix1 = load_index(1);
+
+  // ---- first request touching the segment: number of requests ending at or
+  // before seg_lo (a coarse-then-fine search over kv_indptr[1..B], 64 samples
+  // per round; requests with no tokens are skipped by construction).
+  int cur_b;
+  {
+    int lo = 0, n = p.B;
+    while (n > 64) {
+      const int stride = (n + 63) / 64;
+      const int j = lo + lane * stride;
+      const bool le = j < lo + n && clamp_tok(p.indptr[j + 1], N) <= seg_lo;
+      const int c = __popcll(__ballot(le));
+      if (c == 0) { n = 0; break; }
+      const int nlo = lo + (c - 1) * stride + 1;
+      n = min(stride - 1, lo + n - nlo);
+      lo = nlo;
+    }
+    if (n > 0) {
+      const bool le = lane < n && clamp_tok(p.indptr[lo + lane + 1], N) <= seg_lo;
+      lo += __popcll(__ballot(le));
+    }
+    cur_b = __builtin_amdgcn_readfirstlane(lo);
+  }
+  // window of kv_indptr values: lane j holds indptr[win + j]
+  int win = cur_b;
+  int win_val = clamp_tok(p.indptr[min(win + lane, p.B)], N);
+  auto indptr_at = [&](int b) -> int {
+    if (b - win > 63) {
+      win = b;
+      win_val = clamp_tok(p.indptr[min(win + lane, p.B)], N);
+    }
+    return __builtin_amdgcn_readlane(win_val, b - win);
+  };
+
+  load_rows(ix0, kb0);
+  int32_t ix2 = load_index(2);
+  load_rows(ix1, kb1);
+
+  int req_lo = 0, req_hi = 0;
+  if (cur_b < p.B) {
+    req_lo = indptr_at(cur_b);
+    req_hi = indptr_at(cur_b + 1);
+  }
+
+  // ---- query operand (B of the score MFMA), staged once per workgroup in
+  // LDS in operand order: q_lds[2i+e][lane (t, g)] = q[head t][64i + 16g +
+  // 8e .. +8], the same d-order as the K operand.  Reloaded when the request
+  // changes; the caller guarantees no wave still reads the previous query.
+  int q_b = -1;
+  auto load_q = [&](int b) {
+    for (int c = threadIdx.x; c < 2 * KCHUNKS * 64; c += THREADS) {
+      const int s = c >> 6, l = c & 63;
+      const int h = hg * HEADS + (l & 15);
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (h < p.H) {
+        const int d = 64 * (s >> 1) + 16 * (l >> 4) + 8 * (s & 1);
+        v = *reinterpret_cast<const u32x4_t*>(p.q + ((int64_t)b * p.H + h) * KV_WIDTH + d);
+      }
+      q_lds[s][l] = v;
+    }
+    __syncthreads();
+    q_b = b;
+  };
+
+  // ---- transposed value reads.  For P.V step st (tokens 32st..32st+31)
+  // lane i of group g supplies row 32st + 4g + i/2 (i/2 < 4, wave 2st's MFMA
+  // rows 4g..4g+3) or row 32st + 16 + 4(g^3) + i/2 - 4 (wave 2st+1's rows
+  // (4g..4g+3)^12): exactly the tokens whose probabilities this lane holds.
+  // Rows of later steps are 32 rows further, an immediate offset.
+  const int tr_row0 = (t >> 1) < 4 ? 4 * g + (t >> 1) : 16 + 4 * (g ^ 3) + (t >> 1) - 4;
+  const int tr_off = tr_row0 * VROW + 8 * (t & 1) + 64 * w;
+  // first tile-relative token of this lane's four score rows (4g..4g+3 of
+  // wave w, XOR 12 on odd waves): a run of 4 consecutive tokens
+  const int s_tok0 = 16 * w + 4 * ((w & 1) ? (g ^ 3) : g);
+
+  f32x4_t O[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_w = 0.f;
+
+  auto run_piece = [&](const u32x4_t (&kb)[KCHUNKS], const uint8_t* vt, int tile_lo, int tile_hi,
+                       int plo, int phi) {
+    // scores: S^T[token row m = 4g + r][head t]
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KCHUNKS; ++i) {
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kb[i][0], kb[i][1]),
+                                                   __builtin_bit_cast(bf16x8_t, q_lds[2 * i][lane]),
+                                                   a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kb[i][2], kb[i][3]),
+                                                   __builtin_bit_cast(bf16x8_t, q_lds[2 * i + 1][lane]),
+                                                   a1, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);  // bound the operands live at once
+    }
+    float s[4];
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = tile_lo + s_tok0 + r;
+      const bool ok = tok >= plo && tok < phi;
+      s[r] = ok ? (a0[r] + a1[r]) * p.score_scale : -INFINITY;
+      lmax = fmaxf(lmax, s[r]);
+    }
+    lmax = wave_max_over_groups(lmax);
+    if (g == 0) mx_lds[w][t] = lmax;
+    __syncthreads();
+    float tmax = mx_lds[0][t];
+#pragma unroll
+    for (int v = 1; v < NWAVES; ++v) tmax = fmaxf(tmax, mx_lds[v][t]);
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) O[c] *= alpha;
+      l_w *= alpha;
+    }
+    m_run = m_new;
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
+    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]);
+    const uint32_t p23 = pack_bf16x2(pr[2], pr[3]);
+    l_w += (bf16_bits_to_f32(p01 & 0xFFFFu) + bf16_bits_to_f32(p01 >> 16)) +
+           (bf16_bits_to_f32(p23 & 0xFFFFu) + bf16_bits_to_f32(p23 >> 16));
+    p_lds[w][lane] = make_uint2(p01, p23);
+    __syncthreads();
+
+    bf16x8_t pb[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const uint2 x = p_lds[2 * st][lane];
+      const uint2 y = p_lds[2 * st + 1][lane];
+      u32x4_t v = {x.x, x.y, y.x, y.y};
+      pb[st] = __builtin_bit_cast(bf16x8_t, v);
+    }
+    // Rows of the tile that belong to another request (or lie past the
+    // segment) get probability 0; their value bytes are also zeroed so that
+    // a NaN in another request's rows cannot leak in through 0 * NaN.
+    const bool mask_v = plo > tile_lo || phi < tile_hi;
+    const uint8_t* vbase = vt + tr_off;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint32_t mlo = 0xFFFFFFFFu, mhi = 0xFFFFFFFFu;
+      if (mask_v) {
+        // bytes jj < 4: tokens 32st + 4g + jj; bytes jj >= 4: 32st + 16 + 4(g^3) + jj - 4
+        mlo = run_mask(tile_lo + 32 * st + 4 * g, plo, phi);
+        mhi = run_mask(tile_lo + 32 * st + 16 + 4 * (g ^ 3), plo, phi);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2_t*)(vbase + 32 * VROW * st + 16 * c));
+        const uint32_t lo = (uint32_t)v.x & mlo;
+        const uint32_t hi = (uint32_t)v.y & mhi;
+        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(lo, hi), pb[st], O[c], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto finish_piece = [&](bool complete) {
+    const float lsum = wave_sum_over_groups(l_w);
+    if (g == 0) l_lds[w][t] = lsum;
+    __syncthreads();
+    float l = 0.f;
+#pragma unroll
+    for (int v = 0; v < NWAVES; ++v) l += l_lds[v][t];
+    if (complete) {
+      if (head < p.H) {
+        const float inv = p.kv_scale / l;
+        uint16_t* op = p.out + ((int64_t)cur_b * p.H + head) * V_WIDTH + 64 * w + 4 * g;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint2 v;
+          v.x = pack_bf16x2(O[c][0] * inv, O[c][1] * inv);
+          v.y = pack_bf16x2(O[c][2] * inv, O[c][3] * inv);
+          *reinterpret_cast<uint2*>(op + 16 * c) = v;
+        }
+      }
+    } else {
+      const int64_t piece = (int64_t)(seg + cur_b) * p.Hp + head;
+      const float inv = 1.0f / l;
+      float* op = p.part_o + piece * V_WIDTH + 64 * w + 4 * g;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<float4*>(op + 16 * c) =
+            make_float4(O[c][0] * inv, O[c][1] * inv, O[c][2] * inv, O[c][3] * inv);
+      if (w == 0 && g == 0) p.part_lse[piece] = m_run + __builtin_amdgcn_logf(l);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    l_w = 0.f;
+    m_run = -INFINITY;
+  };
+
+  auto process_tile = [&](int k, u32x4_t (&kb)[KCHUNKS]) {
+    const int tile_lo = seg_lo + k * TILE;
+    const int tile_hi = min(tile_lo + TILE, seg_hi);
+    if (tile_hi - tile_lo < TILE && tile_lo + krow >= tile_hi) {
+#pragma unroll
+      for (int i = 0; i < KCHUNKS; ++i) kb[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    uint8_t* vt = v_lds + (k & 1) * VTILE_BYTES;
+    u32x4_t* vw = reinterpret_cast<u32x4_t*>(vt + krow * VROW + 16 * g);
+#pragma unroll
+    for (int i = 0; i < V_WIDTH / 64; ++i) vw[4 * i] = kb[i];
+    int pos = tile_lo;
+    while (pos < tile_hi) {
+      while (req_hi <= pos && cur_b < p.B) {
+        ++cur_b;
+        req_lo = req_hi;
+        req_hi = cur_b < p.B ? max(req_lo, indptr_at(cur_b + 1)) : req_lo;
+      }
+      if (cur_b >= p.B) break;  // malformed kv_indptr: tokens past the last request
+      const int plo = pos;
+      const int phi = min(tile_hi, req_hi);
+      if (q_b != cur_b) load_q(cur_b);
+      run_piece(kb, vt, tile_lo, tile_hi, plo, phi);
+      if (phi == req_hi || phi == seg_hi) finish_piece(req_lo >= seg_lo && req_hi <= seg_hi);
+      pos = phi;
+    }
+  };
+
+  // ---- main loop: a three-slot register ring, two tiles in flight.
+  for (int k = 0; k < ntiles; k += 3) {
+    ix0 = load_index(k + 3);
+    load_rows(ix2, kb2);
+    process_tile(k, kb0);
+    if (k + 1 >= ntiles) break;
+    ix1 = load_index(k + 4);
+    load_rows(ix0, kb0);
+    process_tile(k + 1, kb1);
+    if (k + 2 >= ntiles) break;
+    ix2 = load_index(k + 5);
+    load_rows(ix1, kb1);
+    process_tile(k + 2, kb2);
+  }
+}
+
+// One wave per (request, head): merges the partials of a request that spans
+// several segments.  out = scale * sum_s w_s o_s / sum_s w_s with
+// w_s = 2^(lse_s - max lse).  Requests with no tokens get zeros; requests
+// inside one segment were written by the split kernel.
+__global__ __launch_bounds__(256) void mla_combine_kernel(const CombineParams p) {
+  const int b = blockIdx.x;
+  const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (head >= p.H) return;
+  const int N = p.total_tokens;
+  const int lo = clamp_tok(p.indptr[b], N);
+  const int hi = max(lo, clamp_tok(p.indptr[b + 1], N));
+  uint16_t* op = p.out + ((int64_t)b * p.H + head) * V_WIDTH + 8 * lane;
+  if (hi <= lo) {
+    *reinterpret_cast<uint4*>(op) = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
+  const int s0 = lo / p.seg_len;
+  const int s1 = (hi - 1) / p.seg_len;
+  if (s0 == s1) return;
+  float M = -INFINITY;
+  for (int s = s0; s <= s1; ++s) M = fmaxf(M, p.part_lse[(int64_t)(s + b) * p.Hp + head]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int s = s0; s <= s1; ++s) {
+    const int64_t piece = (int64_t)(s + b) * p.Hp + head;
+    const float wgt = __builtin_amdgcn_exp2f(p.part_lse[piece] - M);
+    const float4* po = reinterpret_cast<const float4*>(p.part_o + piece * V_WIDTH + 8 * lane);
+    const float4 x = po[0], y = po[1];
+    acc[0] += wgt * x.x; acc[1] += wgt * x.y; acc[2] += wgt * x.z; acc[3] += wgt * x.w;
+    acc[4] += wgt * y.x; acc[5] += wgt * y.y; acc[6] += wgt * y.z; acc[7] += wgt * y.w;
+    den += wgt;
+  }
+  const float inv = p.kv_scale / den;
+  uint4 v;
+  v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<uint4*>(op) = v;
+}
+
+}  // namespace
+
+DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_tokens, int num_cus) {
+  DecodePlan pl{};
+  pl.HG = (num_heads + HEADS - 1) / HEADS;
+  pl.Hp = pl.HG * HEADS;
+  if (total_tokens <= 0) return pl;
+  // one 8-wave workgroup per compute unit in flight; head groups of a segment
+  // are separate workgroups that share the segment's rows through L2
+  int64_t nseg_target = num_cus / pl.HG;
+  if (nseg_target < 1) nseg_target = 1;
+  int64_t seg = (total_tokens + nseg_target - 1) / nseg_target;
+  seg = (seg + TILE - 1) / TILE * TILE;
+  pl.seg_len = (int32_t)seg;
+  pl.nseg = (int32_t)((total_tokens + seg - 1) / seg);
+  pl.items = pl.nseg * pl.HG;
+  if (pl.HG > 1) {
+    pl.xcd_per = (pl.items + 7) / 8;
+    pl.grid = 8 * pl.xcd_per;
+  } else {
+    pl.xcd_per = pl.items;
+    pl.grid = pl.items;
+  }
+  const size_t npieces = (size_t)pl.nseg + (size_t)batch;
+  const size_t o_bytes = npieces * pl.Hp * V_WIDTH * sizeof(float);
+  const size_t lse_bytes = npieces * pl.Hp * sizeof(float);
+  pl.lse_offset = (o_bytes + 255) / 256 * 256;
+  pl.workspace_bytes = pl.lse_offset + (lse_bytes + 255) / 256 * 256;
+  return pl;
+}
+
+hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                             const int32_t* kv_indptr, const int32_t* kv_indices,
+                             int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
+                             float sm_scale, uint16_t* out, void* workspace, const DecodePlan& pl,
+                             hipStream_t stream) {
+  float* part_o = reinterpret_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + pl.lse_offset);
+  if (total_tokens > 0) {
+    SplitParams sp;
+    sp.q = q;
+    sp.pool = kv_pool;
+    sp.indptr = kv_indptr;
+    sp.indices = kv_indices;
+    sp.out = out;
+    sp.part_o = part_o;
+    sp.part_lse = part_lse;
+    sp.max_slot = (uint32_t)(num_slots - 1);
+    sp.total_tokens = (int32_t)total_tokens;
+    sp.B = batch;
+    sp.H = num_heads;
+    sp.HG = pl.HG;
+    sp.Hp = pl.Hp;
+    sp.seg_len = pl.seg_len;
+    sp.items = pl.items;
+    sp.xcd_per = pl.xcd_per;
+    sp.score_scale = (float)((double)sm_scale * (double)scale * 1.4426950408889634);
+    sp.kv_scale = scale;
+    hipLaunchKernelGGL(mla_split_kernel, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  CombineParams cp;
+  cp.indptr = kv_indptr;
+  cp.part_o = part_o;
+  cp.part_lse = part_lse;
+  cp.out = out;
+  cp.total_tokens = (int32_t)total_tokens;
+  cp.B = batch;
+  cp.H = num_heads;
+  cp.Hp = pl.Hp;
+  cp.seg_len = pl.seg_len > 0 ? pl.seg_len : 1;
+  cp.kv_scale = scale;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(batch, (num_heads + 3) / 4), dim3(256), 0, stream, cp);
+  return hipGetLastError();
+}
+
+}  // namespace fp8mla

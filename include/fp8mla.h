@@ -1,0 +1,143 @@
+/*
+ * fp8mla.h -- C ABI of libfp8mla.so: MLA decode attention that reads a paged
+ * FP8-E4M3FN latent KV cache directly, plus the two cast paths it replaces.
+ * Hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * Source of the operations (the pages are three public write-ups):
+ *  - "The KV Cache Cast Bottleneck: A Surgical Fix for 69% Decode Overhead"
+ *    (magik.net), sections The Context and The Message: a per-layer KV pool
+ *    [num_slots, 1, 576] of Float8_e4m3fn, 576 = 512 latent (kv_lora_rank)
+ *    + 64 rope (qk_rope_head_dim), cast in full to BFloat16 with .to() on
+ *    every decode step before an MLA kernel that reads only the slots named
+ *    by kv_indices; the fix is an attention kernel that reads FP8 directly.
+ *  - "The Gather-Then-Cast Pivot" (magik.net), Reasoning Process and
+ *    Assumptions: gather only the active FP8 rows into a compact buffer, cast
+ *    that, and run BF16 attention over sequential indices.
+ *  - "When a Faster Kernel Doesn't Speed Up Serving: Profiling FP8 KV Cache
+ *    on AMD Instinct MI308X" (ROCm blog), Step 3 (CastFromFP8): the same
+ *    FP8->BF16 history cast on the extend path.
+ *
+ * Conventions for every call:
+ *  - All tensor arguments are DEVICE pointers on the current HIP device,
+ *    owned by the caller, row-major and contiguous, 16-byte aligned.  The
+ *    library never allocates or frees device memory and keeps no state
+ *    between calls beyond a per-device compute-unit count.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue kernels on it and return; they never synchronise.  Kernel
+ *    faults surface as errors of a later HIP call, as usual in HIP.
+ *  - FP8 means OCP E4M3FN bytes (bias 7, max 448, NaN = 0x7F/0xFF, no inf).
+ *    BF16 means raw bfloat16 bit patterns (uint16_t).
+ *  - Every argument is checked on the host before any HIP call; a bad
+ *    argument returns a negative status and launches nothing.  There is no
+ *    silent fallback to another path.
+ *  - Slot indices are the caller's contract (0 <= index < num_slots).  The
+ *    kernels clamp every index into the pool, so an out-of-range index gives
+ *    a wrong row, never an out-of-bounds access.
+ */
+#ifndef FP8MLA_H
+#define FP8MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8MLA_KV_WIDTH 576   /* latent row: 512 latent + 64 rope           */
+#define FP8MLA_V_WIDTH 512    /* value operand = first 512 columns of a row */
+#define FP8MLA_MAX_HEADS 256  /* query heads sharing the single KV head     */
+
+/* Status codes (0 = success, negative = error). */
+#define FP8MLA_OK 0
+#define FP8MLA_ERR_NULL_PTR (-1)        /* a required pointer is NULL                     */
+#define FP8MLA_ERR_BAD_SHAPE (-2)       /* a size is negative, zero where not allowed, or too large */
+#define FP8MLA_ERR_MISALIGNED (-3)      /* a tensor pointer is not 16-byte aligned         */
+#define FP8MLA_ERR_WORKSPACE (-4)       /* workspace NULL or smaller than required         */
+#define FP8MLA_ERR_BAD_SCALAR (-5)      /* scale or sm_scale not finite, or scale <= 0     */
+#define FP8MLA_ERR_HIP (-6)             /* a HIP runtime call or kernel launch failed      */
+
+/*
+ * cast_pool_fp8_bf16 -- the full-pool cast the pages measured
+ * ("The KV Cache Cast Bottleneck", The Context: get_key_buffer(l).to(q.dtype)
+ * on a [495552, 1, 576] Float8_e4m3fn pool, every layer, every step).
+ *
+ *   out[i, j] = bf16(e4m3fn(pool[i, j]))   for 0 <= i < num_slots, 0 <= j < 576
+ *
+ * A pure dtype cast, no scale.  Exact: every finite E4M3FN value is a BF16
+ * value; -0 keeps its sign; both NaN codes give 0x7FC0.
+ *   pool      uint8  [num_slots, 576]   read
+ *   out       uint16 [num_slots, 576]   written (must not overlap pool)
+ *   num_slots >= 0 (0 is a no-op)
+ */
+int cast_pool_fp8_bf16(const uint8_t* pool, int64_t num_slots, uint16_t* out, void* stream);
+
+/*
+ * gather_cast_fp8_bf16 -- gather-then-cast fallback
+ * ("The Gather-Then-Cast Pivot", Reasoning Process: k_fp8[kv_indices], cast
+ * of the compact buffer, then attention over sequential indices 0..n-1).
+ *
+ *   out[r, j] = bf16(e4m3fn(pool[indices[r], j]))   for 0 <= r < n
+ *
+ *   pool      uint8  [num_slots, 576]   read
+ *   indices   int32  [n]                slot ids, each in [0, num_slots)
+ *   out       uint16 [n, 576]           written, compact and in index order
+ *   n >= 0 (0 is a no-op); num_slots >= 1 when n > 0
+ */
+int gather_cast_fp8_bf16(const uint8_t* pool, int64_t num_slots, const int32_t* indices,
+                         int64_t n, uint16_t* out, void* stream);
+
+/*
+ * mla_decode_fp8 -- fused MLA decode over the paged FP8 latent cache
+ * (the fix of "The KV Cache Cast Bottleneck", The Message: the attention
+ * kernel reads FP8 and computes in BF16 internally; only the slots named by
+ * kv_indices are ever read, dequantised in-kernel).
+ *
+ * For request b (tokens kv_indices[kv_indptr[b] .. kv_indptr[b+1]-1]) and
+ * query head h, with K[t,:] = scale * e4m3fn(kv_pool[slot_t, :]):
+ *   s[t]        = sm_scale * sum_{d<576} q[b,h,d] * K[t,d]
+ *   out[b,h,:]  = sum_t softmax(s)[t] * K[t, 0:512]          (BF16, round-to-nearest-even)
+ * A request with no tokens gets a zero row.  All heads share one KV head.
+ *
+ *   q           uint16 [batch, num_heads, 576]  BF16 queries
+ *   kv_pool     uint8  [num_slots, 576]         E4M3FN latent rows
+ *   kv_indptr   int32  [batch + 1]              kv_indptr[0] = 0, non-decreasing,
+ *                                               kv_indptr[batch] = total_tokens
+ *   kv_indices  int32  [total_tokens]           token slot ids (page size 1; a paged
+ *                                               layout is expressed slot by slot)
+ *   scale       per-tensor KV dequantisation factor (> 0; 1.0 = plain E4M3 values)
+ *   sm_scale    softmax scale, e.g. 1/sqrt(192)
+ *   out         uint16 [batch, num_heads, 512]  BF16 output, written
+ *   workspace   device scratch of at least mla_decode_fp8_workspace_bytes(...)
+ *               bytes, owned by the caller; contents need no initialisation and
+ *               are garbage afterwards.  Two calls in flight at once on
+ *               different streams need different workspaces.
+ *   1 <= batch, 1 <= num_heads <= FP8MLA_MAX_HEADS, total_tokens >= 0,
+ *   num_slots >= 1 (unless total_tokens == 0).
+ * Work is split into equal token segments over all compute units
+ * (flash-decoding split-K) and merged by a second kernel; the host never
+ * reads kv_indptr, so the call stays asynchronous.
+ */
+int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                   const int32_t* kv_indptr, const int32_t* kv_indices, int64_t total_tokens,
+                   int32_t batch, int32_t num_heads, float scale, float sm_scale,
+                   uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace size in bytes for mla_decode_fp8 on the CURRENT device with these
+ * sizes.  Returns 0 for invalid sizes.  Host-only except for one query of
+ * the device's compute-unit count (cached per device).
+ */
+size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens);
+
+/* Static description of a status code; never NULL. */
+const char* fp8mla_status_string(int status);
+
+/* ABI version of this library (bumped on incompatible changes). */
+int fp8mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8MLA_H */

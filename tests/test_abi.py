@@ -1,0 +1,143 @@
+"""The C ABI loads, exports every symbol the header declares, and rejects bad
+arguments on the host before touching any device (no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8mla.h")
+
+fm = pytest.importorskip("fp8_paged_mla_amd")
+
+
+def _lib():
+    try:
+        return fm.library()
+    except RuntimeError as e:  # not built
+        pytest.fail(str(e))
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+
+
+def _status(name):
+    text = open(HEADER).read()
+    return int(re.search(r"#define %s \((-?\d+)\)|#define %s (-?\d+)" % (name, name), text)
+               .group(1) or 0)
+
+
+def test_header_declares_the_three_calls():
+    names = set(_declared_functions())
+    assert {"mla_decode_fp8", "gather_cast_fp8_bf16", "cast_pool_fp8_bf16"} <= names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = _lib()
+    assert lib.fp8mla_abi_version() == 1
+    for code in range(0, -7, -1):
+        s = fm.status_string(code)
+        assert s and s != "unknown status"
+    assert fm.status_string(12345) == "unknown status"
+
+
+P16 = 4096           # fake, 16-byte aligned, never dereferenced
+P8 = 4096 + 8        # fake, misaligned
+NULL = None
+
+ERR_NULL = -1
+ERR_SHAPE = -2
+ERR_ALIGN = -3
+ERR_SCALAR = -5
+
+
+def test_header_status_values():
+    assert _status("FP8MLA_ERR_NULL_PTR") == ERR_NULL
+    assert _status("FP8MLA_ERR_BAD_SHAPE") == ERR_SHAPE
+    assert _status("FP8MLA_ERR_MISALIGNED") == ERR_ALIGN
+    assert _status("FP8MLA_ERR_BAD_SCALAR") == ERR_SCALAR
+
+
+def test_cast_pool_validation():
+    lib = _lib()
+    assert lib.cast_pool_fp8_bf16(P16, -1, P16, NULL) == ERR_SHAPE
+    assert lib.cast_pool_fp8_bf16(P16, 1 << 33, P16, NULL) == ERR_SHAPE
+    assert lib.cast_pool_fp8_bf16(P16, 0, P16, NULL) == 0          # empty pool: no-op
+    assert lib.cast_pool_fp8_bf16(NULL, 4, P16, NULL) == ERR_NULL
+    assert lib.cast_pool_fp8_bf16(P16, 4, NULL, NULL) == ERR_NULL
+    assert lib.cast_pool_fp8_bf16(P8, 4, P16, NULL) == ERR_ALIGN
+    assert lib.cast_pool_fp8_bf16(P16, 4, P8, NULL) == ERR_ALIGN
+
+
+def test_gather_cast_validation():
+    lib = _lib()
+    assert lib.gather_cast_fp8_bf16(P16, 10, P16, -1, P16, NULL) == ERR_SHAPE
+    assert lib.gather_cast_fp8_bf16(P16, 10, P16, 0, P16, NULL) == 0   # n = 0: no-op
+    assert lib.gather_cast_fp8_bf16(P16, 0, P16, 3, P16, NULL) == ERR_SHAPE
+    assert lib.gather_cast_fp8_bf16(NULL, 10, P16, 3, P16, NULL) == ERR_NULL
+    assert lib.gather_cast_fp8_bf16(P16, 10, NULL, 3, P16, NULL) == ERR_NULL
+    assert lib.gather_cast_fp8_bf16(P16, 10, P16, 3, NULL, NULL) == ERR_NULL
+    assert lib.gather_cast_fp8_bf16(P16, 10, P16 + 2, 3, P16, NULL) == ERR_ALIGN
+    assert lib.gather_cast_fp8_bf16(P16, 10, P16, 3, P8, NULL) == ERR_ALIGN
+
+
+def _decode(lib, **kw):
+    a = dict(q=P16, pool=P16, slots=100, indptr=P16, indices=P16, total=10, B=2, H=16,
+             scale=1.0, sm=0.07, out=P16, ws=P16, ws_bytes=1 << 20, stream=NULL)
+    a.update(kw)
+    return lib.mla_decode_fp8(a["q"], a["pool"], a["slots"], a["indptr"], a["indices"],
+                              a["total"], a["B"], a["H"], a["scale"], a["sm"], a["out"],
+                              a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_mla_decode_validation():
+    lib = _lib()
+    assert _decode(lib, B=0) == ERR_SHAPE
+    assert _decode(lib, H=0) == ERR_SHAPE
+    assert _decode(lib, H=257) == ERR_SHAPE
+    assert _decode(lib, total=-1) == ERR_SHAPE
+    assert _decode(lib, total=1 << 31) == ERR_SHAPE
+    assert _decode(lib, slots=0) == ERR_SHAPE
+    assert _decode(lib, slots=-5) == ERR_SHAPE
+    assert _decode(lib, scale=0.0) == ERR_SCALAR
+    assert _decode(lib, scale=-1.0) == ERR_SCALAR
+    assert _decode(lib, scale=math.nan) == ERR_SCALAR
+    assert _decode(lib, sm=math.inf) == ERR_SCALAR
+    assert _decode(lib, q=NULL) == ERR_NULL
+    assert _decode(lib, out=NULL) == ERR_NULL
+    assert _decode(lib, indptr=NULL) == ERR_NULL
+    assert _decode(lib, pool=NULL) == ERR_NULL
+    assert _decode(lib, indices=NULL) == ERR_NULL
+    assert _decode(lib, ws=NULL) == ERR_NULL
+    assert _decode(lib, q=P8) == ERR_ALIGN
+    assert _decode(lib, out=P8) == ERR_ALIGN
+    assert _decode(lib, pool=P8) == ERR_ALIGN
+    assert _decode(lib, ws=P8) == ERR_ALIGN
+    assert _decode(lib, indptr=P16 + 2) == ERR_ALIGN
+
+
+def test_workspace_query_rejects_bad_sizes():
+    lib = _lib()
+    assert lib.mla_decode_fp8_workspace_bytes(0, 16, 10) == 0
+    assert lib.mla_decode_fp8_workspace_bytes(1, 0, 10) == 0
+    assert lib.mla_decode_fp8_workspace_bytes(1, 300, 10) == 0
+    assert lib.mla_decode_fp8_workspace_bytes(1, 16, -1) == 0
+    assert lib.mla_decode_fp8_workspace_bytes(4, 16, 0) == 0       # nothing to split
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    pool = torch.zeros((4, 576), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        fm.cast_pool_fp8_bf16(pool)

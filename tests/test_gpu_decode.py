@@ -1,0 +1,150 @@
+"""GPU parity of the fused FP8 MLA decode against the float64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import assert_attention_close, attention_errors, bf16_bits, oracle_args
+
+pytestmark = pytest.mark.gpu
+
+fm = pytest.importorskip("fp8_paged_mla_amd")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _run(w):
+    out = fm.mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_full(w, label):
+    out = _run(w)
+    ref = oracle.mla_decode_ref(*oracle_args(w))
+    return assert_attention_close(out, ref, label)
+
+
+def test_config1_tiny(dev):
+    e = _check_full(workloads.config(1, device=dev), "config1")
+    print("config1", e)
+
+
+@pytest.mark.parametrize("H", [1, 8, 16, 17, 32, 64, 128])
+def test_head_counts(dev, H):
+    w = workloads.small(3, H, [1, 130, 37], seed=H, device=dev)
+    _check_full(w, "H=%d" % H)
+
+
+@pytest.mark.parametrize("lengths", [
+    [1], [2], [127], [128], [129], [255, 1, 3], [0, 5, 0], [64] * 7, [1] * 40,
+])
+def test_ragged_lengths(dev, lengths):
+    w = workloads.small(len(lengths), 16, lengths, seed=len(lengths) + sum(lengths), device=dev)
+    _check_full(w, str(lengths))
+
+
+def test_all_requests_empty(dev):
+    w = workloads.small(4, 16, [0, 0, 0, 0], num_slots=64, device=dev)
+    out = _run(w)
+    assert torch.count_nonzero(out.float()).item() == 0
+
+
+def test_requests_span_many_segments(dev):
+    # 3000 + 50 + 9000 tokens -> many segments per request, exercising the combine
+    w = workloads.small(3, 16, [3000, 50, 9000], seed=11, device=dev, scale=1.7)
+    e = _check_full(w, "multi-segment")
+    print("multi-segment", e)
+
+
+@pytest.mark.parametrize("page_size", [16, 64])
+def test_paged_layout(dev, page_size):
+    w = workloads.small(5, 32, [700, 64, 65, 1, 2049], page_size=page_size, seed=page_size,
+                        device=dev)
+    _check_full(w, "page=%d" % page_size)
+
+
+def test_large_scores_and_outliers(dev):
+    # saturated +-448 values and a large q: near one-hot softmax
+    w = workloads.small(2, 16, [300, 1000], seed=5, device=dev, q_sigma=4.0, outlier_frac=0.02)
+    _check_full(w, "outliers")
+
+
+def test_query_zero_gives_mean(dev):
+    w = workloads.small(2, 16, [333, 20], seed=6, device=dev)
+    w.q.zero_()
+    _check_full(w, "q=0")
+
+
+def test_nan_rows_do_not_leak_across_requests(dev):
+    # request 1's rows contain NaN codes; request 0 (sharing a 128-token tile) must stay exact
+    w = workloads.small(2, 16, [50, 40], seed=7, device=dev)
+    idx1 = w.indices[50:90].long()
+    w.pool[idx1, 5] = 0x7F
+    out = _run(w)
+    args = oracle_args(w)
+    ref0 = oracle.mla_decode_ref(*args, requests=[0])
+    assert_attention_close(out[0:1], ref0, "nan isolation")
+    assert torch.isnan(out[1].float()).any()
+
+
+def test_deterministic(dev):
+    w = workloads.small(3, 16, [900, 17, 2000], seed=8, device=dev)
+    a = _run(w)
+    b = _run(w)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_slot_relocation_invariance(dev):
+    w = workloads.small(2, 16, [400, 300], seed=9, device=dev)
+    a = _run(w)
+    g = torch.Generator().manual_seed(0)
+    perm = torch.randperm(w.num_slots, generator=g).to(dev)
+    moved = torch.empty_like(w.pool)
+    moved[perm] = w.pool
+    w2 = workloads.Workload(w.name, w.seed, w.B, w.H, w.page_size, w.num_slots, w.lengths, moved,
+                            w.indptr, perm[w.indices.long()].to(torch.int32).contiguous(), w.q,
+                            w.scale, w.sm_scale)
+    b = _run(w2)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def _sampled(w, requests, label):
+    out = _run(w)
+    ref = oracle.mla_decode_ref(*oracle_args(w), requests=requests)
+    e = assert_attention_close(out[requests], ref, label)
+    print(label, requests, e)
+    return out
+
+
+def test_config2_batch40_sampled(dev):
+    w = workloads.config(2, device=dev)
+    L = w.lengths
+    req = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, 17, 39})
+    _sampled(w, req, "config2")
+
+
+def test_config3_layer_full(dev):
+    w = workloads.config(3, device=dev)
+    _check_full(w, "config3")
+
+
+def test_config4_long_context_sampled(dev):
+    w = workloads.config(4, device=dev)
+    L = w.lengths
+    _sampled(w, [int(np.argmin(L)), int(np.argmax(L))], "config4")
+
+
+def test_config5_serving_mix_sampled(dev):
+    w = workloads.config(5, device=dev)
+    L = w.lengths
+    req = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, 100, 255})
+    _sampled(w, req, "config5")
