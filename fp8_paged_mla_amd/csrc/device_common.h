@@ -11,6 +11,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
 
 constexpr int KV_WIDTH = 576;  // bytes per latent row: 512 latent + 64 rope
 constexpr int V_WIDTH = 512;   // value operand = first 512 columns
@@ -41,6 +42,9 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // the way of cached data).
 __device__ __forceinline__ u32x4_t load16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ u32x2_t load8_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
 }
 __device__ __forceinline__ void store16_nt(void* p, u32x4_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));

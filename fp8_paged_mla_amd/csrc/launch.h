@@ -19,7 +19,7 @@ hipError_t launch_gather_cast(const uint8_t* pool, int64_t num_slots, const int3
 struct DecodePlan {
   int32_t HG;          // head groups of 16
   int32_t Hp;          // padded head count = 16 * HG
-  int32_t seg_len;     // tokens per segment (multiple of the 128-token tile)
+  int32_t seg_len;     // tokens per segment
   int32_t nseg;        // number of segments
   int32_t items;       // nseg * HG workgroups doing work
   int32_t xcd_per;     // work items per XCD slot of the launch grid

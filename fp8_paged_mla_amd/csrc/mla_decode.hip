@@ -49,6 +49,7 @@ constexpr int HEADS = 16;                         // heads per workgroup
 constexpr int VROW = V_WIDTH + 16;                // LDS bytes per value row (odd 16B-chunk stride)
 constexpr int VTILE_BYTES = TILE * VROW;          // 67584
 constexpr int KCHUNKS = KV_WIDTH / 64;            // 9 x 16-byte chunks per lane per row
+constexpr int QPIECES = 2 * KCHUNKS * 64;         // 16-byte pieces of one head group's query
 
 struct SplitParams {
   const uint16_t* q;
@@ -110,6 +111,57 @@ __device__ __forceinline__ uint32_t run_mask(int base, int lo, int hi) {
   return (uint32_t)(upto_b & ~below_a);
 }
 
+// ---- explicitly pipelined loads.  The row and index loads of the tile
+// pipeline are issued as inline assembly and waited for with an explicit
+// s_waitcnt vmcnt(N): left to itself the compiler sinks prefetches down to
+// their first use (or drains every load at the loop head), which removes the
+// overlap the register ring exists for.  Vector-memory operations complete
+// in issue order, so "at most N outstanding" proves every older load done.
+// After a wait, pin() makes the compiler treat the registers as redefined
+// there, so no use of the data can be scheduled above the wait.
+__device__ __forceinline__ int32_t issue_load_i32(const int32_t* p) {
+  int32_t v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+
+__device__ __forceinline__ void issue_load_row(u32x4_t (&kb)[9], const uint8_t* rp) {
+  asm volatile(
+      "global_load_dwordx4 %0, %9, off nt\n\t"
+      "global_load_dwordx4 %1, %9, off offset:64 nt\n\t"
+      "global_load_dwordx4 %2, %9, off offset:128 nt\n\t"
+      "global_load_dwordx4 %3, %9, off offset:192 nt\n\t"
+      "global_load_dwordx4 %4, %9, off offset:256 nt\n\t"
+      "global_load_dwordx4 %5, %9, off offset:320 nt\n\t"
+      "global_load_dwordx4 %6, %9, off offset:384 nt\n\t"
+      "global_load_dwordx4 %7, %9, off offset:448 nt\n\t"
+      "global_load_dwordx4 %8, %9, off offset:512 nt"
+      : "=&v"(kb[0]), "=&v"(kb[1]), "=&v"(kb[2]), "=&v"(kb[3]), "=&v"(kb[4]), "=&v"(kb[5]),
+        "=&v"(kb[6]), "=&v"(kb[7]), "=&v"(kb[8])
+      : "v"(rp));
+}
+
+__device__ __forceinline__ u32x4_t issue_load_16(const void* p) {
+  u32x4_t v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
+}
+
+__device__ __forceinline__ void pin(u32x4_t (&kb)[9]) {
+  asm volatile(""
+               : "+v"(kb[0]), "+v"(kb[1]), "+v"(kb[2]), "+v"(kb[3]), "+v"(kb[4]), "+v"(kb[5]),
+                 "+v"(kb[6]), "+v"(kb[7]), "+v"(kb[8]));
+}
+
+__device__ __forceinline__ void pin(int32_t& x) { asm volatile("" : "+v"(x)); }
+
+__device__ __forceinline__ void pin(u32x4_t& x) { asm volatile("" : "+v"(x)); }
+
 // Token row (tile-relative) held by MFMA row m of wave w.  Odd waves use
 // row m ^ 12 so that the transposed LDS reads of two consecutive waves'
 // rows fall in distinct banks.
@@ -138,23 +190,29 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   if (seg_lo >= seg_hi) return;
   const int ntiles = (seg_hi - seg_lo + TILE - 1) / TILE;
   const int head = hg * HEADS + t;  // head whose scores / outputs this lane carries
+  // Query operand piece c of 1152 (step s = c / 64, lane l = c % 64): 8 bf16
+  // of head hg*16 + l%16 at d = 64(s/2) + 16(l/16) + 8(s%2); element offset
+  // into q (heads >= H read the last head and are zeroed when stored).
+  auto q_piece_offset = [&](int b, int c) -> int64_t {
+    const int s = c >> 6, l = c & 63;
+    const int h = min(hg * HEADS + (l & 15), p.H - 1);
+    const int d = 64 * (s >> 1) + 16 * (l >> 4) + 8 * (s & 1);
+    return ((int64_t)b * p.H + h) * KV_WIDTH + d;
+  };
 
   // ---- token rows: lane loads row krow of every tile
   const int krow = tile_row(w, t);
-  // Loads in the pipelined loop are unconditional (a branch around them
-  // makes the compiler drain every outstanding load at the join).  A lane
-  // whose token lies past the segment reads the segment's first row instead
-  // -- a cache hit on a line another lane fetches -- and process_tile zeroes
-  // that lane's data.
+  // Loads in the pipelined loop are unconditional (no branch around an
+  // in-flight load).  A lane whose token lies past the segment reads the
+  // segment's first row instead -- a cache hit on a line another lane
+  // fetches -- and process_tile zeroes that lane's data.
   auto load_index = [&](int k) -> int32_t {
     const int tok = seg_lo + k * TILE + krow;
-    return p.indices[tok < seg_hi ? tok : seg_lo];
+    return issue_load_i32(p.indices + (tok < seg_hi ? tok : seg_lo));
   };
   auto load_rows = [&](int32_t idx, u32x4_t (&kb)[KCHUNKS]) {
     const uint32_t s = (uint32_t)idx < p.max_slot ? (uint32_t)idx : p.max_slot;
-    const uint8_t* rp = p.pool + (uint64_t)s * KV_WIDTH + 16 * g;
-#pragma unroll
-    for (int i = 0; i < KCHUNKS; ++i) kb[i] = load16_nt(rp + 64 * i);
+    issue_load_row(kb, p.pool + (uint64_t)s * KV_WIDTH + 16 * g);
   };
 
   u32x4_t kb0[KCHUNKS], kb1[KCHUNKS], kb2[KCHUNKS];
@@ -162,10 +220,17 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   int32_t ix1 = load_index(1);
 
   // ---- first request touching the segment: number of requests ending at or
-  // before seg_lo (a coarse-then-fine search over kv_indptr[1..B], 64 samples
-  // per round; requests with no tokens are skipped by construction).
+  // before seg_lo.  Lane j of a 64-entry window holds kv_indptr[win + j];
+  // for batches up to 63 one load covers the whole array, otherwise a
+  // coarse-then-fine search over kv_indptr[1..B] (64 samples per round) runs
+  // first.  Requests with no tokens are skipped by construction.
   int cur_b;
-  {
+  int win = 0;
+  int win_val;
+  if (p.B <= 63) {
+    win_val = clamp_tok(p.indptr[min(lane, p.B)], N);
+    cur_b = __popcll(__ballot(lane >= 1 && lane <= p.B && win_val <= seg_lo));
+  } else {
     int lo = 0, n = p.B;
     while (n > 64) {
       const int stride = (n + 63) / 64;
@@ -182,10 +247,9 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       lo += __popcll(__ballot(le));
     }
     cur_b = __builtin_amdgcn_readfirstlane(lo);
+    win = cur_b;
+    win_val = clamp_tok(p.indptr[min(win + lane, p.B)], N);
   }
-  // window of kv_indptr values: lane j holds indptr[win + j]
-  int win = cur_b;
-  int win_val = clamp_tok(p.indptr[min(win + lane, p.B)], N);
   auto indptr_at = [&](int b) -> int {
     if (b - win > 63) {
       win = b;
@@ -194,6 +258,21 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     return __builtin_amdgcn_readlane(win_val, b - win);
   };
 
+  wait_vm<0>();
+  pin(ix0);
+  pin(ix1);
+  // The first request's query: three 16-byte pieces per thread of the
+  // 1152-piece operand layout (see load_q), fetched together with the first
+  // two tiles and written to LDS at the first tile.
+  u32x4_t q0v[3];
+  {
+    const int b0 = min(cur_b, p.B - 1);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int c = threadIdx.x + j * THREADS < QPIECES ? threadIdx.x + j * THREADS : threadIdx.x;
+      q0v[j] = issue_load_16(p.q + q_piece_offset(b0, c));
+    }
+  }
   load_rows(ix0, kb0);
   int32_t ix2 = load_index(2);
   load_rows(ix1, kb1);
@@ -210,19 +289,34 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   // changes; the caller guarantees no wave still reads the previous query.
   int q_b = -1;
   auto load_q = [&](int b) {
-    for (int c = threadIdx.x; c < 2 * KCHUNKS * 64; c += THREADS) {
-      const int s = c >> 6, l = c & 63;
-      const int h = hg * HEADS + (l & 15);
+    for (int c = threadIdx.x; c < QPIECES; c += THREADS) {
       u32x4_t v = {0u, 0u, 0u, 0u};
-      if (h < p.H) {
-        const int d = 64 * (s >> 1) + 16 * (l >> 4) + 8 * (s & 1);
-        v = *reinterpret_cast<const u32x4_t*>(p.q + ((int64_t)b * p.H + h) * KV_WIDTH + d);
-      }
-      q_lds[s][l] = v;
+      if (hg * HEADS + ((c & 63) & 15) < p.H)
+        v = *reinterpret_cast<const u32x4_t*>(p.q + q_piece_offset(b, c));
+      q_lds[c >> 6][c & 63] = v;
     }
     __syncthreads();
     q_b = b;
   };
+  // first request's query, prefetched in the prologue
+  auto store_q0 = [&]() {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      pin(q0v[j]);
+      const int c = threadIdx.x + j * THREADS;
+      if (c < QPIECES) {
+        u32x4_t v = q0v[j];
+        if (hg * HEADS + ((c & 63) & 15) >= p.H) v = u32x4_t{0u, 0u, 0u, 0u};
+        q_lds[c >> 6][c & 63] = v;
+      }
+    }
+    __syncthreads();
+    q_b = cur_b;
+  };
+  // The query loads were issued before the rows of tiles 0 and 1 (9 + 1 + 9
+  // operations): waiting for 19 outstanding retires the query only.
+  wait_vm<19>();
+  if (cur_b < p.B) store_q0();
 
   // ---- transposed value reads.  For P.V step st (tokens 32st..32st+31)
   // lane i of group g supplies row 32st + 4g + i/2 (i/2 < 4, wave 2st's MFMA
@@ -384,26 +478,43 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     }
   };
 
-  // ---- main loop: a three-slot register ring, two tiles in flight.
+  // ---- main loop: a three-slot register ring, two tiles in flight.  Issue
+  // order per tile k: index of tile k+3, then (once the index of tile k+2 is
+  // in) the rows of tile k+2.  Before the rows of k+2 are issued, at most 10
+  // operations may be outstanding -- the rows of k+1 and the index of k+3 --
+  // which proves both the index of k+2 and the rows of tile k have arrived.
   for (int k = 0; k < ntiles; k += 3) {
     ix0 = load_index(k + 3);
+    wait_vm<10>();
+    pin(ix2);
+    pin(kb0);
     load_rows(ix2, kb2);
     process_tile(k, kb0);
     if (k + 1 >= ntiles) break;
     ix1 = load_index(k + 4);
+    wait_vm<10>();
+    pin(ix0);
+    pin(kb1);
     load_rows(ix0, kb0);
     process_tile(k + 1, kb1);
     if (k + 2 >= ntiles) break;
     ix2 = load_index(k + 5);
+    wait_vm<10>();
+    pin(ix1);
+    pin(kb2);
     load_rows(ix1, kb1);
     process_tile(k + 2, kb2);
   }
+  wait_vm<0>();  // retire prefetches issued past the last tile
 }
 
 // One wave per (request, head): merges the partials of a request that spans
 // several segments.  out = scale * sum_s w_s o_s / sum_s w_s with
 // w_s = 2^(lse_s - max lse).  Requests with no tokens get zeros; requests
-// inside one segment were written by the split kernel.
+// inside one segment were written by the split kernel.  The log-sum-exps of
+// up to 64 pieces are loaded in one wave-wide step and the partial outputs
+// four pieces at a time, so a request costs one or two memory latencies, not
+// one per piece.
 __global__ __launch_bounds__(256) void mla_combine_kernel(const CombineParams p) {
   const int b = blockIdx.x;
   const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -420,18 +531,44 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const CombineParams p)
   const int s0 = lo / p.seg_len;
   const int s1 = (hi - 1) / p.seg_len;
   if (s0 == s1) return;
+  const int np = s1 - s0 + 1;
+  const float* lse = p.part_lse + (int64_t)(s0 + b) * p.Hp + head;  // piece i at lse[i * Hp]
   float M = -INFINITY;
-  for (int s = s0; s <= s1; ++s) M = fmaxf(M, p.part_lse[(int64_t)(s + b) * p.Hp + head]);
+  for (int i = lane; i < np; i += 64) M = fmaxf(M, lse[(int64_t)i * p.Hp]);
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int s = s0; s <= s1; ++s) {
-    const int64_t piece = (int64_t)(s + b) * p.Hp + head;
-    const float wgt = __builtin_amdgcn_exp2f(p.part_lse[piece] - M);
-    const float4* po = reinterpret_cast<const float4*>(p.part_o + piece * V_WIDTH + 8 * lane);
-    const float4 x = po[0], y = po[1];
-    acc[0] += wgt * x.x; acc[1] += wgt * x.y; acc[2] += wgt * x.z; acc[3] += wgt * x.w;
-    acc[4] += wgt * y.x; acc[5] += wgt * y.y; acc[6] += wgt * y.z; acc[7] += wgt * y.w;
-    den += wgt;
+  const float* po = p.part_o + ((int64_t)(s0 + b) * p.Hp + head) * V_WIDTH + 8 * lane;
+  const int64_t pstride = (int64_t)p.Hp * V_WIDTH;  // floats between consecutive pieces
+  for (int base = 0; base < np; base += 64) {
+    const int cnt = min(64, np - base);
+    const float wl = lane < cnt ? __builtin_amdgcn_exp2f(lse[(int64_t)(base + lane) * p.Hp] - M) : 0.f;
+    int i = 0;
+    for (; i + 4 <= cnt; i += 4) {
+      float4 x[4], y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4* q = reinterpret_cast<const float4*>(po + (int64_t)(base + i + u) * pstride);
+        x[u] = q[0];
+        y[u] = q[1];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i + u));
+        acc[0] += wgt * x[u].x; acc[1] += wgt * x[u].y; acc[2] += wgt * x[u].z; acc[3] += wgt * x[u].w;
+        acc[4] += wgt * y[u].x; acc[5] += wgt * y[u].y; acc[6] += wgt * y[u].z; acc[7] += wgt * y[u].w;
+        den += wgt;
+      }
+    }
+    for (; i < cnt; ++i) {
+      const float4* q = reinterpret_cast<const float4*>(po + (int64_t)(base + i) * pstride);
+      const float4 x = q[0], y = q[1];
+      const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i));
+      acc[0] += wgt * x.x; acc[1] += wgt * x.y; acc[2] += wgt * x.z; acc[3] += wgt * x.w;
+      acc[4] += wgt * y.x; acc[5] += wgt * y.y; acc[6] += wgt * y.z; acc[7] += wgt * y.w;
+      den += wgt;
+    }
   }
   const float inv = p.kv_scale / den;
   uint4 v;
@@ -453,8 +590,9 @@ DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_token
   // are separate workgroups that share the segment's rows through L2
   int64_t nseg_target = num_cus / pl.HG;
   if (nseg_target < 1) nseg_target = 1;
-  int64_t seg = (total_tokens + nseg_target - 1) / nseg_target;
-  seg = (seg + TILE - 1) / TILE * TILE;
+  // Segments need no alignment (tiles are counted from each segment's start),
+  // so the token stream is cut into exactly nseg_target pieces when it can be.
+  const int64_t seg = (total_tokens + nseg_target - 1) / nseg_target;
   pl.seg_len = (int32_t)seg;
   pl.nseg = (int32_t)((total_tokens + seg - 1) / seg);
   pl.items = pl.nseg * pl.HG;
