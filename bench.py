@@ -39,7 +39,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--layers", type=int, default=78, help="config 3: layers per decode step")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -130,6 +131,10 @@ def main():
     fm.library()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+
+    if args.config == 3:
+        print(json.dumps(cast_path_step(fm, workloads, torch, dev, args)), flush=True)
+        return
 
     base = workloads.config(args.config, 0, device=dev)
     pool_bytes = base.pool.numel()
@@ -222,6 +227,63 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(base)
     print(json.dumps(result), flush=True)
+
+
+def cast_path_step(fm, workloads, torch, dev, args):
+    """The pages' per-step comparison over `layers` distinct 495,552-slot FP8
+    pools (one request, 4,096 tokens, 64 heads): full-pool cast, gather-cast of
+    the active slots, and the fused decode, each summed over the layers.  The
+    BF16 attention that follows a cast on the pages is not included; the
+    numbers are the cast kernels' own time."""
+    L = args.layers
+    w0 = workloads.config(3, 0, device=dev)
+    pools = [w0.pool] + [workloads.random_pool(495552, seed=3000 + 7 * l + 1, device=dev)
+                         for l in range(1, L)]
+    stream = torch.cuda.current_stream(dev)
+    cast_out = torch.empty((495552, 576), dtype=torch.bfloat16, device=dev)
+    g_out = torch.empty((w0.total_tokens, 576), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w0.B, w0.H, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(256, fm.mla_decode_fp8_workspace_bytes(w0.B, w0.H, w0.total_tokens)),
+                     dtype=torch.uint8, device=dev)
+
+    def timed(fn, reps=3):
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize(dev)
+            e0.record(stream)
+            for l in range(L):
+                fn(pools[l])
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    for l in range(L):  # warm-up pass
+        fm.cast_pool_fp8_bf16(pools[l], out=cast_out)
+    cast_ms = timed(lambda p: fm.cast_pool_fp8_bf16(p, out=cast_out))
+    gather_ms = timed(lambda p: fm.gather_cast_fp8_bf16(p, w0.indices, out=g_out))
+    fused_ms = timed(lambda p: fm.mla_decode_fp8(w0.q, p, w0.indptr, w0.indices, w0.scale,
+                                                 w0.sm_scale, out=out, workspace=ws))
+    cast_bytes = 495552 * 576 * 3
+    gather_bytes = w0.total_tokens * (4 + 576 + 1152)
+    return {
+        "metric": "per-decode-step time over %d layers: full-pool cast vs gather-cast vs fused" % L,
+        "unit": "ms/step",
+        "higher_is_better": False,
+        "data": "synthetic",
+        "config": {"workload": workloads.CONFIG_NAMES[3], "layers": L,
+                   "pool_bytes_total_GB": round(L * 495552 * 576 / 1e9, 2)},
+        "cast_pool_ms_per_step": round(cast_ms, 3),
+        "cast_pool_GBps": round(L * cast_bytes / (cast_ms * 1e-3) / 1e9, 1),
+        "cast_pool_pct_hbm_peak": round(100 * L * cast_bytes / (cast_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 1),
+        "gather_cast_ms_per_step": round(gather_ms, 4),
+        "gather_cast_GBps": round(L * gather_bytes / (gather_ms * 1e-3) / 1e9, 1),
+        "gather_cast_us_per_layer": round(gather_ms * 1e3 / L, 2),
+        "fused_decode_ms_per_step": round(fused_ms, 4),
+        "fused_decode_us_per_layer": round(fused_ms * 1e3 / L, 2),
+    }
 
 
 def secondary(fm, reps, outs, wss, stream, dev, args):

@@ -46,9 +46,9 @@ constexpr int NWAVES = 8;
 constexpr int THREADS = 64 * NWAVES;              // 512
 constexpr int TILE = 16 * NWAVES;                 // tokens per tile: 16 per wave
 constexpr int HEADS = 16;                         // heads per workgroup
-constexpr int VROW = V_WIDTH + 16;                // LDS bytes per value row (odd 16B-chunk stride)
-constexpr int VTILE_BYTES = TILE * VROW;          // 67584
-constexpr int KCHUNKS = KV_WIDTH / 64;            // 9 x 16-byte chunks per lane per row
+constexpr int ROWB = KV_WIDTH + 16;               // LDS bytes per row: 37 16-byte slots (odd stride)
+constexpr int TILE_BYTES = TILE * ROWB;           // 75776
+constexpr int KCHUNKS = KV_WIDTH / 64;            // 16-byte loads per lane per tile; query steps / 2
 constexpr int QPIECES = 2 * KCHUNKS * 64;         // 16-byte pieces of one head group's query
 
 struct SplitParams {
@@ -125,26 +125,76 @@ __device__ __forceinline__ int32_t issue_load_i32(const int32_t* p) {
   return v;
 }
 
-__device__ __forceinline__ void issue_load_row(u32x4_t (&kb)[9], const uint8_t* rp) {
+__device__ __forceinline__ void issue_load_rows(u32x4_t (&kb)[9], const uint8_t* const (&a)[9]) {
   asm volatile(
       "global_load_dwordx4 %0, %9, off nt\n\t"
-      "global_load_dwordx4 %1, %9, off offset:64 nt\n\t"
-      "global_load_dwordx4 %2, %9, off offset:128 nt\n\t"
-      "global_load_dwordx4 %3, %9, off offset:192 nt\n\t"
-      "global_load_dwordx4 %4, %9, off offset:256 nt\n\t"
-      "global_load_dwordx4 %5, %9, off offset:320 nt\n\t"
-      "global_load_dwordx4 %6, %9, off offset:384 nt\n\t"
-      "global_load_dwordx4 %7, %9, off offset:448 nt\n\t"
-      "global_load_dwordx4 %8, %9, off offset:512 nt"
+      "global_load_dwordx4 %1, %10, off nt\n\t"
+      "global_load_dwordx4 %2, %11, off nt\n\t"
+      "global_load_dwordx4 %3, %12, off nt\n\t"
+      "global_load_dwordx4 %4, %13, off nt\n\t"
+      "global_load_dwordx4 %5, %14, off nt\n\t"
+      "global_load_dwordx4 %6, %15, off nt\n\t"
+      "global_load_dwordx4 %7, %16, off nt\n\t"
+      "global_load_dwordx4 %8, %17, off nt"
       : "=&v"(kb[0]), "=&v"(kb[1]), "=&v"(kb[2]), "=&v"(kb[3]), "=&v"(kb[4]), "=&v"(kb[5]),
         "=&v"(kb[6]), "=&v"(kb[7]), "=&v"(kb[8])
-      : "v"(rp));
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "v"(a[8]));
+}
+
+// Query operand of one lane: 9 pairs of 16-byte pieces 64 elements (128
+// bytes) apart.
+__device__ __forceinline__ void issue_load_q(bf16x8_t (&q)[18], const uint16_t* qp) {
+  asm volatile(
+      "global_load_dwordx4 %0, %18, off\n\t"
+      "global_load_dwordx4 %1, %18, off offset:16\n\t"
+      "global_load_dwordx4 %2, %18, off offset:128\n\t"
+      "global_load_dwordx4 %3, %18, off offset:144\n\t"
+      "global_load_dwordx4 %4, %18, off offset:256\n\t"
+      "global_load_dwordx4 %5, %18, off offset:272\n\t"
+      "global_load_dwordx4 %6, %18, off offset:384\n\t"
+      "global_load_dwordx4 %7, %18, off offset:400\n\t"
+      "global_load_dwordx4 %8, %18, off offset:512\n\t"
+      "global_load_dwordx4 %9, %18, off offset:528\n\t"
+      "global_load_dwordx4 %10, %18, off offset:640\n\t"
+      "global_load_dwordx4 %11, %18, off offset:656\n\t"
+      "global_load_dwordx4 %12, %18, off offset:768\n\t"
+      "global_load_dwordx4 %13, %18, off offset:784\n\t"
+      "global_load_dwordx4 %14, %18, off offset:896\n\t"
+      "global_load_dwordx4 %15, %18, off offset:912\n\t"
+      "global_load_dwordx4 %16, %18, off offset:1024\n\t"
+      "global_load_dwordx4 %17, %18, off offset:1040"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]),
+        "=&v"(q[7]), "=&v"(q[8]), "=&v"(q[9]), "=&v"(q[10]), "=&v"(q[11]), "=&v"(q[12]),
+        "=&v"(q[13]), "=&v"(q[14]), "=&v"(q[15]), "=&v"(q[16]), "=&v"(q[17])
+      : "v"(qp));
+}
+
+__device__ __forceinline__ void pin_q(bf16x8_t (&q)[18]) {
+  asm volatile(""
+               : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]),
+                 "+v"(q[6]), "+v"(q[7]), "+v"(q[8]));
+  asm volatile(""
+               : "+v"(q[9]), "+v"(q[10]), "+v"(q[11]), "+v"(q[12]), "+v"(q[13]), "+v"(q[14]),
+                 "+v"(q[15]), "+v"(q[16]), "+v"(q[17]));
 }
 
 __device__ __forceinline__ u32x4_t issue_load_16(const void* p) {
   u32x4_t v;
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p));
   return v;
+}
+
+// Global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
+// address lds_base + 16*l (lds_base wave-uniform, passed in M0).  Issued as
+// inline assembly so that the compiler neither drains it at barriers nor
+// waits for it before unrelated LDS reads; the caller waits with vmcnt.
+// M0 is not otherwise used by these kernels.
+__device__ __forceinline__ void issue_lds_dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
 }
 
 template <int N>
@@ -168,11 +218,12 @@ __device__ __forceinline__ void pin(u32x4_t& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ int tile_row(int w, int m) { return 16 * w + ((w & 1) ? (m ^ 12) : m); }
 
 __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2 * VTILE_BYTES];
+  // One row tile, the query of the current request, and the softmax exchange.
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[TILE_BYTES];
+  __shared__ u32x4_t q_lds[2][2 * KCHUNKS][64];  // current query and the next request's
   __shared__ float mx_lds[NWAVES][HEADS];
   __shared__ uint2 p_lds[NWAVES][64];
   __shared__ float l_lds[NWAVES][HEADS];
-  __shared__ u32x4_t q_lds[2 * KCHUNKS][64];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -190,34 +241,53 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   if (seg_lo >= seg_hi) return;
   const int ntiles = (seg_hi - seg_lo + TILE - 1) / TILE;
   const int head = hg * HEADS + t;  // head whose scores / outputs this lane carries
-  // Query operand piece c of 1152 (step s = c / 64, lane l = c % 64): 8 bf16
-  // of head hg*16 + l%16 at d = 64(s/2) + 16(l/16) + 8(s%2); element offset
-  // into q (heads >= H read the last head and are zeroed when stored).
-  auto q_piece_offset = [&](int b, int c) -> int64_t {
-    const int s = c >> 6, l = c & 63;
-    const int h = min(hg * HEADS + (l & 15), p.H - 1);
-    const int d = 64 * (s >> 1) + 16 * (l >> 4) + 8 * (s & 1);
-    return ((int64_t)b * p.H + h) * KV_WIDTH + d;
-  };
 
-  // ---- token rows: lane loads row krow of every tile
-  const int krow = tile_row(w, t);
-  // Loads in the pipelined loop are unconditional (no branch around an
-  // in-flight load).  A lane whose token lies past the segment reads the
-  // segment's first row instead -- a cache hit on a line another lane
-  // fetches -- and process_tile zeroes that lane's data.
+  // ---- loads.  Wave w fetches rows 16w..16w+15 of each tile.  Its 16 x 36
+  // chunks of 16 bytes are numbered P = 36*r + c and lane l takes P = 64j + l
+  // in load j (j < 9): each load instruction reads whole rows back to back
+  // (one contiguous run per row, ~1.8 rows per instruction), the pattern that
+  // gathers random 576-byte rows fastest.  Lanes r < 16 (and their copies at
+  // r + 16k) hold the slot id of row r; each load gets its row's slot with a
+  // cross-lane permute.  A lane whose token lies past the segment reads the
+  // segment's first row instead (a cache hit); its scores and value bytes
+  // are masked out.
+  auto opaque_lane = [&]() -> int {  // recomputed per use, not kept across the loop
+    int l = lane;
+    asm volatile("" : "+v"(l));
+    return l;
+  };
   auto load_index = [&](int k) -> int32_t {
-    const int tok = seg_lo + k * TILE + krow;
+    const int tok = seg_lo + k * TILE + 16 * w + t;
     return issue_load_i32(p.indices + (tok < seg_hi ? tok : seg_lo));
   };
   auto load_rows = [&](int32_t idx, u32x4_t (&kb)[KCHUNKS]) {
-    const uint32_t s = (uint32_t)idx < p.max_slot ? (uint32_t)idx : p.max_slot;
-    issue_load_row(kb, p.pool + (uint64_t)s * KV_WIDTH + 16 * g);
+    const uint8_t* a[KCHUNKS];
+    const int ln = opaque_lane();
+#pragma unroll
+    for (int j = 0; j < KCHUNKS; ++j) {
+      const int P = 64 * j + ln;
+      const int r = P / KV_CHUNKS;
+      const int c = P - r * KV_CHUNKS;
+      const uint32_t s = (uint32_t)__shfl(idx, r);
+      a[j] = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
+    }
+    issue_load_rows(kb, a);
+  };
+  // stage a tile's rows (this wave's 16) into the LDS row tile
+  auto store_rows = [&](const u32x4_t (&kb)[KCHUNKS]) {
+    const int ln = opaque_lane();
+#pragma unroll
+    for (int j = 0; j < KCHUNKS; ++j) {
+      const int P = 64 * j + ln;
+      const int r = P / KV_CHUNKS;
+      *reinterpret_cast<u32x4_t*>(kv_lds + (16 * w + r) * ROWB + 16 * (P - r * KV_CHUNKS)) = kb[j];
+    }
   };
 
   u32x4_t kb0[KCHUNKS], kb1[KCHUNKS], kb2[KCHUNKS];
   int32_t ix0 = load_index(0);
   int32_t ix1 = load_index(1);
+  int32_t ix2 = load_index(2);
 
   // ---- first request touching the segment: number of requests ending at or
   // before seg_lo.  Lane j of a 64-entry window holds kv_indptr[win + j];
@@ -258,73 +328,117 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     return __builtin_amdgcn_readlane(win_val, b - win);
   };
 
-  wait_vm<0>();
-  pin(ix0);
-  pin(ix1);
-  // The first request's query: three 16-byte pieces per thread of the
-  // 1152-piece operand layout (see load_q), fetched together with the first
-  // two tiles and written to LDS at the first tile.
-  u32x4_t q0v[3];
-  {
-    const int b0 = min(cur_b, p.B - 1);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int c = threadIdx.x + j * THREADS < QPIECES ? threadIdx.x + j * THREADS : threadIdx.x;
-      q0v[j] = issue_load_16(p.q + q_piece_offset(b0, c));
-    }
-  }
-  load_rows(ix0, kb0);
-  int32_t ix2 = load_index(2);
-  load_rows(ix1, kb1);
-
   int req_lo = 0, req_hi = 0;
   if (cur_b < p.B) {
     req_lo = indptr_at(cur_b);
     req_hi = indptr_at(cur_b + 1);
   }
 
-  // ---- query operand (B of the score MFMA), staged once per workgroup in
-  // LDS in operand order: q_lds[2i+e][lane (t, g)] = q[head t][64i + 16g +
-  // 8e .. +8], the same d-order as the K operand.  Reloaded when the request
-  // changes; the caller guarantees no wave still reads the previous query.
-  int q_b = -1;
-  auto load_q = [&](int b) {
-    for (int c = threadIdx.x; c < QPIECES; c += THREADS) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (hg * HEADS + ((c & 63) & 15) < p.H)
-        v = *reinterpret_cast<const u32x4_t*>(p.q + q_piece_offset(b, c));
-      q_lds[c >> 6][c & 63] = v;
-    }
-    __syncthreads();
-    q_b = b;
+  // ---- query operand (B of the score MFMA), staged once per workgroup in LDS
+  // in operand order: piece c = 64s + l holds, for step s = 2i+e and lane
+  // l = (t, g), q[head t][64i + 16g + 8e .. +8] -- the d-order in which lane
+  // (t, g) reads its K row.  Heads >= H read the last head and are zeroed.
+  auto q_piece_offset = [&](int b, int c) -> int64_t {
+    const int s = c >> 6, l = c & 63;
+    const int h = min(hg * HEADS + (l & 15), p.H - 1);
+    const int d = 64 * (s >> 1) + 16 * (l >> 4) + 8 * (s & 1);
+    return ((int64_t)b * p.H + h) * KV_WIDTH + d;
   };
-  // first request's query, prefetched in the prologue
-  auto store_q0 = [&]() {
+  int qsel = 0;  // which q_lds buffer holds the current query
+  auto store_q_piece = [&](int c, u32x4_t v) {
+    if (hg * HEADS + ((c & 63) & 15) >= p.H) v = u32x4_t{0u, 0u, 0u, 0u};
+    q_lds[qsel][c >> 6][c & 63] = v;
+  };
+
+  wait_vm<0>();
+  pin(ix0);
+  pin(ix1);
+  pin(ix2);
+  // Prologue: only the first request's query (3 pieces per thread) and the
+  // rows of tile 0 are requested before computing starts.  Every workgroup
+  // starts at once; had tiles 1 and 2 been requested too, tile 0 would queue
+  // behind three tiles' worth of traffic from the whole GPU.
+  {
+    u32x4_t q0v[3];
+    const int b0 = min(cur_b, p.B - 1);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int c = threadIdx.x + j * THREADS < QPIECES ? threadIdx.x + j * THREADS : threadIdx.x;
+      q0v[j] = issue_load_16(p.q + q_piece_offset(b0, c));
+    }
+    load_rows(ix0, kb0);
+    wait_vm<0>();
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       pin(q0v[j]);
       const int c = threadIdx.x + j * THREADS;
-      if (c < QPIECES) {
-        u32x4_t v = q0v[j];
-        if (hg * HEADS + ((c & 63) & 15) >= p.H) v = u32x4_t{0u, 0u, 0u, 0u};
-        q_lds[c >> 6][c & 63] = v;
+      if (c < QPIECES) store_q_piece(c, q0v[j]);
+    }
+    pin(kb0);
+    store_rows(kb0);
+  }
+  int q_b = cur_b;
+  __syncthreads();
+  // Then, in the main loop's order ("index of j+1 before rows of j"): index of
+  // tile 3, rows of tiles 1 and 2.
+  ix0 = load_index(3);
+  load_rows(ix1, kb1);
+  load_rows(ix2, kb2);
+  // Request switch inside the segment: reload the query (compiler-managed
+  // loads).  Every wave has passed the barriers of the previous piece, so no
+  // one still reads the old query.
+  auto load_q = [&](int b) {
+    for (int c = threadIdx.x; c < QPIECES; c += THREADS) store_q_piece(c, *reinterpret_cast<const u32x4_t*>(p.q + q_piece_offset(b, c)));
+    __syncthreads();
+    q_b = b;
+  };
+  // Next request's query, copied into the idle q_lds buffer one tile ahead
+  // of the switch.  Called at a tile's top between the index load and the row
+  // loads: the next tile's "at most 10 outstanding" wait then proves the copy
+  // landed, since it sits between two operations that wait already covers.
+  // Heads >= H get the last head's values (their outputs are never written).
+  int pref_b = -1;
+  auto maybe_prefetch_q = [&](int k) {
+    if (pref_b >= 0 || cur_b + 1 >= p.B) return;
+    const int nlo = seg_lo + (k + 1) * TILE;
+    const int nhi = min(nlo + TILE, seg_hi);
+    if (req_hi < nlo || req_hi >= nhi) return;  // the switch is not in tile k+1
+    const int nb = cur_b + 1;
+    if (indptr_at(nb + 1) <= req_hi) return;  // next request empty: slow path
+    const uint32_t qbase = (uint32_t)(uintptr_t)(
+        (__attribute__((address_space(3))) u32x4_t*)&q_lds[qsel ^ 1][0][0]);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (j < 2 || w < 2) {  // 1152 pieces = 2 x 512 + 128
+        const int c = THREADS * j + 64 * w + lane;
+        issue_lds_dma16(p.q + q_piece_offset(nb, c),
+                        __builtin_amdgcn_readfirstlane(qbase + 16 * (THREADS * j + 64 * w)));
       }
     }
-    __syncthreads();
-    q_b = cur_b;
+    pref_b = nb;
   };
-  // The query loads were issued before the rows of tiles 0 and 1 (9 + 1 + 9
-  // operations): waiting for 19 outstanding retires the query only.
-  wait_vm<19>();
-  if (cur_b < p.B) store_q0();
+  auto switch_q = [&](int b) {
+    if (pref_b == b) {  // every wave's copy has landed (see maybe_prefetch_q)
+      __syncthreads();
+      qsel ^= 1;
+      q_b = b;
+    } else {
+      load_q(b);
+    }
+    pref_b = -1;
+  };
 
-  // ---- transposed value reads.  For P.V step st (tokens 32st..32st+31)
-  // lane i of group g supplies row 32st + 4g + i/2 (i/2 < 4, wave 2st's MFMA
-  // rows 4g..4g+3) or row 32st + 16 + 4(g^3) + i/2 - 4 (wave 2st+1's rows
+
+  // ---- LDS read offsets.  Score operand: lane (t, g) reads chunk 4i + g
+  // (bytes 64i + 16g .. +16) of MFMA row t, i.e. tile row tile_row(w, t).
+  const int k_off = tile_row(w, t) * ROWB + 16 * g;
+  // Transposed value reads.  For P.V step st (tokens 32st..32st+31) lane i
+  // of group g supplies row 32st + 4g + i/2 (i/2 < 4, wave 2st's MFMA rows
+  // 4g..4g+3) or row 32st + 16 + 4(g^3) + i/2 - 4 (wave 2st+1's rows
   // (4g..4g+3)^12): exactly the tokens whose probabilities this lane holds.
   // Rows of later steps are 32 rows further, an immediate offset.
   const int tr_row0 = (t >> 1) < 4 ? 4 * g + (t >> 1) : 16 + 4 * (g ^ 3) + (t >> 1) - 4;
-  const int tr_off = tr_row0 * VROW + 8 * (t & 1) + 64 * w;
+  const int tr_off = tr_row0 * ROWB + 8 * (t & 1) + 64 * w;
   // first tile-relative token of this lane's four score rows (4g..4g+3 of
   // wave w, XOR 12 on odd waves): a run of 4 consecutive tokens
   const int s_tok0 = 16 * w + 4 * ((w & 1) ? (g ^ 3) : g);
@@ -334,20 +448,24 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   for (int c = 0; c < 4; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   float l_w = 0.f;
+  i32x2_t vt[4][4];  // value operand of the current tile, read once per tile
 
-  auto run_piece = [&](const u32x4_t (&kb)[KCHUNKS], const uint8_t* vt, int tile_lo, int tile_hi,
-                       int plo, int phi) {
-    // scores: S^T[token row m = 4g + r][head t]
+  // One piece (the part of a tile that belongs to one request).  When
+  // `next` is non-null this is the tile's last piece: after the max exchange
+  // (every wave is past its reads of the row tile) the next tile's rows are
+  // staged, and the probability exchange barrier publishes them.
+  auto run_piece = [&](int tile_lo, int plo, int phi, u32x4_t* next) {
     f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* kp = kv_lds + k_off;
 #pragma unroll
     for (int i = 0; i < KCHUNKS; ++i) {
-      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kb[i][0], kb[i][1]),
-                                                   __builtin_bit_cast(bf16x8_t, q_lds[2 * i][lane]),
+      const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(kp + 64 * i);
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv[0], kv[1]),
+                                                   __builtin_bit_cast(bf16x8_t, q_lds[qsel][2 * i][lane]),
                                                    a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kb[i][2], kb[i][3]),
-                                                   __builtin_bit_cast(bf16x8_t, q_lds[2 * i + 1][lane]),
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv[2], kv[3]),
+                                                   __builtin_bit_cast(bf16x8_t, q_lds[qsel][2 * i + 1][lane]),
                                                    a1, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);  // bound the operands live at once
     }
     float s[4];
     float lmax = -INFINITY;
@@ -361,6 +479,15 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     lmax = wave_max_over_groups(lmax);
     if (g == 0) mx_lds[w][t] = lmax;
     __syncthreads();
+    if (next) {
+      // The next tile's rows were issued before 19 or more younger operations
+      // (tile 0: rows of tiles 2 and 3 and an index; later tiles: two tiles'
+      // rows and indices), so "at most 19 outstanding" proves they arrived.
+      u32x4_t (&nk)[KCHUNKS] = *reinterpret_cast<u32x4_t(*)[KCHUNKS]>(next);
+      wait_vm<19>();
+      pin(nk);
+      store_rows(nk);
+    }
     float tmax = mx_lds[0][t];
 #pragma unroll
     for (int v = 1; v < NWAVES; ++v) tmax = fmaxf(tmax, mx_lds[v][t]);
@@ -390,11 +517,10 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       u32x4_t v = {x.x, x.y, y.x, y.y};
       pb[st] = __builtin_bit_cast(bf16x8_t, v);
     }
-    // Rows of the tile that belong to another request (or lie past the
-    // segment) get probability 0; their value bytes are also zeroed so that
-    // a NaN in another request's rows cannot leak in through 0 * NaN.
-    const bool mask_v = plo > tile_lo || phi < tile_hi;
-    const uint8_t* vbase = vt + tr_off;
+    // Rows of the tile outside this piece (another request, or past the
+    // segment) have probability 0; their value bytes are zeroed as well so
+    // that a NaN in another request's rows cannot enter through 0 * NaN.
+    const bool mask_v = plo > tile_lo || phi < tile_lo + TILE;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       uint32_t mlo = 0xFFFFFFFFu, mhi = 0xFFFFFFFFu;
@@ -405,13 +531,10 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) i32x2_t*)(vbase + 32 * VROW * st + 16 * c));
-        const uint32_t lo = (uint32_t)v.x & mlo;
-        const uint32_t hi = (uint32_t)v.y & mhi;
+        const uint32_t lo = (uint32_t)vt[st][c].x & mlo;
+        const uint32_t hi = (uint32_t)vt[st][c].y & mhi;
         O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(lo, hi), pb[st], O[c], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -450,18 +573,23 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     m_run = -INFINITY;
   };
 
-  auto process_tile = [&](int k, u32x4_t (&kb)[KCHUNKS]) {
+  // Tile k: its rows are in the LDS tile (published by the previous
+  // barrier); `next` holds the rows of tile k+1 in registers (they have
+  // arrived) and is staged during the tile's last piece.
+  auto process_tile = [&](int k, u32x4_t (&next)[KCHUNKS]) {
     const int tile_lo = seg_lo + k * TILE;
     const int tile_hi = min(tile_lo + TILE, seg_hi);
-    if (tile_hi - tile_lo < TILE && tile_lo + krow >= tile_hi) {
+    {
+      const uint8_t* vbase = kv_lds + tr_off;
 #pragma unroll
-      for (int i = 0; i < KCHUNKS; ++i) kb[i] = u32x4_t{0u, 0u, 0u, 0u};
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          vt[st][c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2_t*)(vbase + 32 * ROWB * st + 16 * c));
     }
-    uint8_t* vt = v_lds + (k & 1) * VTILE_BYTES;
-    u32x4_t* vw = reinterpret_cast<u32x4_t*>(vt + krow * VROW + 16 * g);
-#pragma unroll
-    for (int i = 0; i < V_WIDTH / 64; ++i) vw[4 * i] = kb[i];
     int pos = tile_lo;
+    bool staged = false;
     while (pos < tile_hi) {
       while (req_hi <= pos && cur_b < p.B) {
         ++cur_b;
@@ -471,39 +599,62 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       if (cur_b >= p.B) break;  // malformed kv_indptr: tokens past the last request
       const int plo = pos;
       const int phi = min(tile_hi, req_hi);
-      if (q_b != cur_b) load_q(cur_b);
-      run_piece(kb, vt, tile_lo, tile_hi, plo, phi);
+      if (q_b != cur_b) switch_q(cur_b);
+      const bool last = phi == tile_hi;
+      run_piece(tile_lo, plo, phi, last ? &next[0] : nullptr);
+      staged |= last;
       if (phi == req_hi || phi == seg_hi) finish_piece(req_lo >= seg_lo && req_hi <= seg_hi);
       pos = phi;
     }
+    if (!staged) {  // no piece reached the tile end (malformed kv_indptr): keep the barrier count
+      __syncthreads();
+      wait_vm<19>();
+      pin(next);
+      store_rows(next);
+      __syncthreads();
+    }
   };
 
-  // ---- main loop: a three-slot register ring, two tiles in flight.  Issue
-  // order per tile k: index of tile k+3, then (once the index of tile k+2 is
-  // in) the rows of tile k+2.  Before the rows of k+2 are issued, at most 10
-  // operations may be outstanding -- the rows of k+1 and the index of k+3 --
-  // which proves both the index of k+2 and the rows of tile k have arrived.
+  // ---- main loop: a three-slot register ring.  At tile k the rows of tile
+  // k+1 wait in registers to be staged into LDS (after arriving), and the
+  // rows of tiles k+2 and k+3 are in flight.  Issue order per tile: index of
+  // tile k+4, then the rows of tile k+3 once the index of k+3 has arrived --
+  // "at most 10 outstanding" (rows of k+2, index of k+4) proves it, and also
+  // proves the rows of k+1 arrived.  Tile 0 is peeled: there the index of
+  // tile 3 precedes the rows of tiles 1 and 2, so 19 may stay outstanding.
+  // Ring slots: rows of tile j live in kb[j % 3]; indices of tile j in ix[j % 3].
+  ix1 = load_index(4);
+  wait_vm<19>();
+  pin(ix0);
+  maybe_prefetch_q(0);
+  load_rows(ix0, kb0);
+  process_tile(0, kb1);
   for (int k = 0; k < ntiles; k += 3) {
-    ix0 = load_index(k + 3);
-    wait_vm<10>();
-    pin(ix2);
-    pin(kb0);
-    load_rows(ix2, kb2);
-    process_tile(k, kb0);
+    if (k > 0) {
+      ix1 = load_index(k + 4);
+      wait_vm<10>();
+      pin(ix0);
+      pin(kb1);
+      maybe_prefetch_q(k);
+      load_rows(ix0, kb0);
+      process_tile(k, kb1);
+    }
     if (k + 1 >= ntiles) break;
-    ix1 = load_index(k + 4);
-    wait_vm<10>();
-    pin(ix0);
-    pin(kb1);
-    load_rows(ix0, kb0);
-    process_tile(k + 1, kb1);
-    if (k + 2 >= ntiles) break;
     ix2 = load_index(k + 5);
     wait_vm<10>();
     pin(ix1);
     pin(kb2);
+    maybe_prefetch_q(k + 1);
     load_rows(ix1, kb1);
-    process_tile(k + 2, kb2);
+    process_tile(k + 1, kb2);
+    if (k + 2 >= ntiles) break;
+    ix0 = load_index(k + 6);
+    wait_vm<10>();
+    pin(ix2);
+    pin(kb0);
+    maybe_prefetch_q(k + 2);
+    load_rows(ix2, kb2);
+    process_tile(k + 2, kb0);
   }
   wait_vm<0>();  // retire prefetches issued past the last tile
 }
