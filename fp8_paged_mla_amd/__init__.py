@@ -158,6 +158,7 @@ def gather_cast_fp8_bf16(pool: torch.Tensor, indices: torch.Tensor,
 
 def mla_decode_fp8_workspace_bytes(batch: int, num_heads: int, total_tokens: int,
                                    device=None) -> int:
+    """Bytes of workspace mla_decode_fp8 needs (scratch; no initialisation)."""
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     with torch.cuda.device(dev):
         return int(library().mla_decode_fp8_workspace_bytes(int(batch), int(num_heads),

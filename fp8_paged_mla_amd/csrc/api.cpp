@@ -108,7 +108,7 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
   const int cus = current_device_cus();
   if (cus <= 0) return FP8MLA_ERR_HIP;
   const fp8mla::DecodePlan plan = fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus);
-  if (workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
+  if (total_tokens > 0 && workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
   const hipError_t e = fp8mla::launch_mla_decode(q, kv_pool, num_slots, kv_indptr, kv_indices,
                                                  total_tokens, batch, num_heads, scale, sm_scale,
                                                  out, workspace, plan,

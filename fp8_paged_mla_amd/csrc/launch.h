@@ -14,16 +14,16 @@ hipError_t launch_cast_pool(const uint8_t* pool, int64_t num_slots, uint16_t* ou
 hipError_t launch_gather_cast(const uint8_t* pool, int64_t num_slots, const int32_t* indices,
                               int64_t n, uint16_t* out, hipStream_t stream);
 
-// Decode schedule: equal token segments x head groups, and the split-K
-// workspace layout (partial outputs, then log2-sum-exp values).
+// Decode schedule: equal segments of the request-tile list x head groups, and the split-K
+// workspace layout (per-request piece ranges, partial outputs, log2-sum-exp values).
 struct DecodePlan {
   int32_t HG;          // head groups of 16
   int32_t Hp;          // padded head count = 16 * HG
-  int32_t seg_len;     // tokens per segment
-  int32_t nseg;        // number of segments
+  int32_t nseg;        // segments the list of request tiles is cut into
   int32_t items;       // nseg * HG workgroups doing work
   int32_t xcd_per;     // work items per XCD slot of the launch grid
   int32_t grid;        // launched workgroups (>= items)
+  size_t part_o_offset;  // byte offset of the partial outputs inside the workspace
   size_t lse_offset;   // byte offset of the lse array inside the workspace
   size_t workspace_bytes;
 };

@@ -8,32 +8,31 @@
 // Only the rows named by kv_indices are read, and they are dequantised in the
 // kernel: the fix the pages call for instead of the full-pool .to() cast.
 //
-// Work decomposition.  The concatenated token stream of all requests
-// (length N = kv_indptr[B]) is cut into equal segments; one workgroup
-// processes one segment for one group of 16 heads, walking it in tiles of
-// 128 tokens and handling request boundaries inside the tile.  For every
-// request it touches it writes either the final output (request entirely
-// inside the segment) or a partial (o normalised, log2-sum-exp) that the
-// combine kernel merges.  Segments are balanced by tokens, not by request,
-// so long and short requests cost the same per token.
+// Work decomposition.  Every request's token range is cut into tiles of 128
+// tokens counted from the request's start (its last tile may be partial), so
+// no tile mixes two requests.  The concatenated list of all requests' tiles
+// is cut into equal segments, one per compute unit and group of 16 heads:
+// segments are balanced by tiles, not by request, so long and short requests
+// cost the same per token.  For every request it touches a workgroup writes
+// either the final output (request entirely inside the segment) or a partial
+// (o normalised, log2-sum-exp) that the combine kernel merges.
 //
-// Inside a workgroup (8 waves, 16 heads):
-//  * wave w owns tokens [16w, 16w+16) of each tile for the score product
-//    S^T = K q^T (MFMA 16x16x32 bf16, M = 16 tokens, N = 16 heads,
-//    K = 576 in 18 steps).  Its lanes load those tokens' 576-byte rows with
-//    16-byte loads straight into registers, already in MFMA A-operand order
-//    (lane (t, g) holds 16 bytes at offset 64*i + 16*g of row t), two tiles
-//    ahead of use; the FP8 bytes are converted to bf16 right before the MFMA.
-//  * the same registers hold the value part (first 512 bytes) of each row;
-//    they are written once to LDS, where every wave reads the transposed
-//    operand it needs with ds_read_b64_tr_b8.
-//  * the softmax is exchanged through LDS: wave-local maxima, then bf16
-//    probabilities; all waves then share one running maximum per head.
-//  * wave w owns output columns [64w, 64w+64) of the P.V product
-//    O^T = V^T P^T (MFMA 16x16x32 bf16, M = 16 columns, N = 16 heads,
-//    K = 32 tokens), so no cross-wave reduction of O is needed.
-// KV bytes move from HBM exactly once per head group; every value byte is
-// converted once per wave that consumes it.
+// Inside a workgroup (8 waves, 16 heads), per tile:
+//  * the tile's 128 rows are copied global -> LDS by the waves themselves
+//    (global_load_lds, 16 bytes per lane) two tiles ahead of use, into one of
+//    two LDS slots; no registers are held by rows in flight;
+//  * wave w computes the scores of tokens [16w, 16w+16): S^T = K q^T with
+//    MFMA 16x16x32 bf16 (M = 16 tokens, N = 16 heads, K = 576 in 18 steps),
+//    K read from LDS and converted FP8 -> bf16 right before the MFMA, q held
+//    in registers for as long as the request lasts;
+//  * the softmax is exchanged through LDS (wave maxima, then bf16
+//    probabilities) so that all waves share one running maximum per head;
+//  * wave w owns output columns [64w, 64w+64) of O^T = V^T P^T (MFMA
+//    16x16x32 bf16, M = 16 columns, N = 16 heads, K = 32 tokens), reading the
+//    transposed FP8 value operand with ds_read_b64_tr_b8: no cross-wave
+//    reduction of O.
+// KV bytes move from HBM once per head group; each value byte is converted
+// once per wave that consumes it.
 #include "device_common.h"
 #include "launch.h"
 
@@ -45,11 +44,15 @@ namespace {
 constexpr int NWAVES = 8;
 constexpr int THREADS = 64 * NWAVES;              // 512
 constexpr int TILE = 16 * NWAVES;                 // tokens per tile: 16 per wave
+constexpr int TILE_SHIFT = 7;                     // log2(TILE)
 constexpr int HEADS = 16;                         // heads per workgroup
-constexpr int ROWB = KV_WIDTH + 16;               // LDS bytes per row: 37 16-byte slots (odd stride)
+constexpr int ROW_SLOTS = KV_CHUNKS + 1;          // 16-byte LDS slots per row: 36 + 1 pad (odd)
+constexpr int ROWB = 16 * ROW_SLOTS;              // 592 LDS bytes per row
 constexpr int TILE_BYTES = TILE * ROWB;           // 75776
-constexpr int KCHUNKS = KV_WIDTH / 64;            // 16-byte loads per lane per tile; query steps / 2
-constexpr int QPIECES = 2 * KCHUNKS * 64;         // 16-byte pieces of one head group's query
+constexpr int KSTEPS = KV_WIDTH / 64;             // 16-byte K reads per lane per tile; query steps / 2
+constexpr int QSTEPS = 2 * KSTEPS;                // 18 MFMA steps of 32 dims over 576
+constexpr int DMA_OPS = (16 * ROW_SLOTS + 63) / 64;  // LDS-copy ops per wave per tile: 10
+static_assert(TILE == 1 << TILE_SHIFT, "tile size");
 
 struct SplitParams {
   const uint16_t* q;
@@ -59,29 +62,17 @@ struct SplitParams {
   uint16_t* out;
   float* part_o;
   float* part_lse;
+  int2* req_pieces;  // per request: (segment of its first piece, number of pieces)
   uint32_t max_slot;
   int32_t total_tokens;
   int32_t B;
   int32_t H;
   int32_t HG;
   int32_t Hp;
-  int32_t seg_len;
-  int32_t items;
+  int32_t nseg;     // segments the tile list is cut into
+  int32_t items;    // nseg * HG
   int32_t xcd_per;
   float score_scale;  // sm_scale * scale * log2(e): scores in the base-2 domain
-  float kv_scale;
-};
-
-struct CombineParams {
-  const int32_t* indptr;
-  const float* part_o;
-  const float* part_lse;
-  uint16_t* out;
-  int32_t total_tokens;
-  int32_t B;
-  int32_t H;
-  int32_t Hp;
-  int32_t seg_len;
   float kv_scale;
 };
 
@@ -100,51 +91,103 @@ __device__ __forceinline__ float wave_sum_over_groups(float x) {
 
 __device__ __forceinline__ int clamp_tok(int v, int n) { return v < 0 ? 0 : (v > n ? n : v); }
 
-// Byte mask over 4 consecutive tokens base..base+3: 0xFF for each token in
-// [lo, hi), 0 otherwise.
-__device__ __forceinline__ uint32_t run_mask(int base, int lo, int hi) {
-  const int a = min(max(lo - base, 0), 4);
-  const int b = min(max(hi - base, 0), 4);
-  if (b <= a) return 0u;
-  const uint64_t upto_b = (b == 4) ? 0xFFFFFFFFull : ((1ull << (8 * b)) - 1ull);
-  const uint64_t below_a = (1ull << (8 * a)) - 1ull;
-  return (uint32_t)(upto_b & ~below_a);
+// ---- request tiles.  Request b covers tokens [lo_b, hi_b) with
+// lo_b = clamp(kv_indptr[b], 0, N) and hi_b = max(lo_b, clamp(kv_indptr[b+1],
+// 0, N)), and has ceil((hi_b - lo_b) / 128) tiles.
+__device__ __forceinline__ int request_tiles(const int32_t* indptr, int b, int B, int N) {
+  if (b >= B) return 0;
+  const int lo = clamp_tok(indptr[b], N);
+  const int hi = max(lo, clamp_tok(indptr[b + 1], N));
+  return (hi - lo + TILE - 1) >> TILE_SHIFT;
 }
 
-// ---- explicitly pipelined loads.  The row and index loads of the tile
-// pipeline are issued as inline assembly and waited for with an explicit
-// s_waitcnt vmcnt(N): left to itself the compiler sinks prefetches down to
-// their first use (or drains every load at the loop head), which removes the
-// overlap the register ring exists for.  Vector-memory operations complete
-// in issue order, so "at most N outstanding" proves every older load done.
-// After a wait, pin() makes the compiler treat the registers as redefined
-// there, so no use of the data can be scheduled above the wait.
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Merge of the np partial results (pieces s0 + b .. s0 + np - 1 + b) of
+// request b for one head, by one wave: out = scale * sum_s w_s o_s / sum_s
+// w_s with w_s = 2^(lse_s - max lse).  Pieces are taken eight at a time with
+// all their loads issued together (one memory latency per eight pieces) and
+// folded in with a running maximum.  Lane l produces output columns
+// 8l .. 8l+7.
+__device__ __forceinline__ void merge_pieces(const float* part_o, const float* part_lse, int Hp,
+                                             int b, int s0, int np, int head, float kv_scale,
+                                             uint16_t* op, int lane) {
+  const float* lse = part_lse + (int64_t)(s0 + b) * Hp + head;  // piece i at lse[i * Hp]
+  const float* po = part_o + ((int64_t)(s0 + b) * Hp + head) * V_WIDTH + 8 * lane;
+  const int64_t pstride = (int64_t)Hp * V_WIDTH;  // floats between consecutive pieces
+  float M = -INFINITY, den = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < np; base += 8) {
+    const int cnt = min(8, np - base);
+    const float lv = lane < cnt ? lse[(int64_t)(base + lane) * Hp] : -INFINITY;
+    float4 x[8], y[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // u >= cnt re-reads the last piece (in bounds, unused)
+      const float4* q = reinterpret_cast<const float4*>(po + (int64_t)(base + min(u, cnt - 1)) * pstride);
+      x[u] = q[0];
+      y[u] = q[1];
+    }
+    float cm = lv;
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+    const float m_new = fmaxf(M, __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                     __builtin_bit_cast(int, cm))));
+    const float r = __builtin_amdgcn_exp2f(M - m_new);  // 0 on the first chunk
+    den *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= r;
+    M = m_new;
+    const float wl = lane < cnt ? __builtin_amdgcn_exp2f(lv - M) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < cnt) {
+        const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
+        acc[0] += wgt * x[u].x; acc[1] += wgt * x[u].y; acc[2] += wgt * x[u].z; acc[3] += wgt * x[u].w;
+        acc[4] += wgt * y[u].x; acc[5] += wgt * y[u].y; acc[6] += wgt * y[u].z; acc[7] += wgt * y[u].w;
+        den += wgt;
+      }
+    }
+  }
+  const float inv = kv_scale / den;
+  uint4 v;
+  v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<uint4*>(op + 8 * lane) = v;
+}
+
+// ---- explicitly pipelined loads.  Index, query and row loads are issued as
+// inline assembly and waited for with an explicit s_waitcnt vmcnt(N): left to
+// itself the compiler sinks prefetches down to their first use or drains
+// every load at a barrier, which removes the overlap the pipeline exists
+// for.  Loads (register and LDS-destination alike) complete in issue order,
+// so "at most N outstanding" proves every load older than the N youngest
+// done; stores, which the compiler may interleave, only make such a wait
+// stricter.  After a wait, pin() makes the compiler treat the registers as
+// redefined there, so no use of the data can be scheduled above the wait.
 __device__ __forceinline__ int32_t issue_load_i32(const int32_t* p) {
   int32_t v;
   asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p));
   return v;
 }
 
-__device__ __forceinline__ void issue_load_rows(u32x4_t (&kb)[9], const uint8_t* const (&a)[9]) {
-  asm volatile(
-      "global_load_dwordx4 %0, %9, off nt\n\t"
-      "global_load_dwordx4 %1, %10, off nt\n\t"
-      "global_load_dwordx4 %2, %11, off nt\n\t"
-      "global_load_dwordx4 %3, %12, off nt\n\t"
-      "global_load_dwordx4 %4, %13, off nt\n\t"
-      "global_load_dwordx4 %5, %14, off nt\n\t"
-      "global_load_dwordx4 %6, %15, off nt\n\t"
-      "global_load_dwordx4 %7, %16, off nt\n\t"
-      "global_load_dwordx4 %8, %17, off nt"
-      : "=&v"(kb[0]), "=&v"(kb[1]), "=&v"(kb[2]), "=&v"(kb[3]), "=&v"(kb[4]), "=&v"(kb[5]),
-        "=&v"(kb[6]), "=&v"(kb[7]), "=&v"(kb[8])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-        "v"(a[8]));
-}
-
 // Query operand of one lane: 9 pairs of 16-byte pieces 64 elements (128
 // bytes) apart.
-__device__ __forceinline__ void issue_load_q(bf16x8_t (&q)[18], const uint16_t* qp) {
+__device__ __forceinline__ void issue_load_q(bf16x8_t (&q)[QSTEPS], const uint16_t* qp) {
   asm volatile(
       "global_load_dwordx4 %0, %18, off\n\t"
       "global_load_dwordx4 %1, %18, off offset:16\n\t"
@@ -170,7 +213,7 @@ __device__ __forceinline__ void issue_load_q(bf16x8_t (&q)[18], const uint16_t* 
       : "v"(qp));
 }
 
-__device__ __forceinline__ void pin_q(bf16x8_t (&q)[18]) {
+__device__ __forceinline__ void pin_q(bf16x8_t (&q)[QSTEPS]) {
   asm volatile(""
                : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]),
                  "+v"(q[6]), "+v"(q[7]), "+v"(q[8]));
@@ -179,17 +222,10 @@ __device__ __forceinline__ void pin_q(bf16x8_t (&q)[18]) {
                  "+v"(q[15]), "+v"(q[16]), "+v"(q[17]));
 }
 
-__device__ __forceinline__ u32x4_t issue_load_16(const void* p) {
-  u32x4_t v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p));
-  return v;
-}
-
 // Global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
-// address lds_base + 16*l (lds_base wave-uniform, passed in M0).  Issued as
-// inline assembly so that the compiler neither drains it at barriers nor
-// waits for it before unrelated LDS reads; the caller waits with vmcnt.
-// M0 is not otherwise used by these kernels.
+// address lds_base + 16*l (lds_base wave-uniform, passed in M0); lanes
+// outside exec write nothing.  The caller waits with vmcnt.  M0 is not
+// otherwise used by these kernels.
 __device__ __forceinline__ void issue_lds_dma16(const void* g, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                :
@@ -202,25 +238,41 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
 }
 
-__device__ __forceinline__ void pin(u32x4_t (&kb)[9]) {
-  asm volatile(""
-               : "+v"(kb[0]), "+v"(kb[1]), "+v"(kb[2]), "+v"(kb[3]), "+v"(kb[4]), "+v"(kb[5]),
-                 "+v"(kb[6]), "+v"(kb[7]), "+v"(kb[8]));
+// Wait until at most n vector-memory operations are outstanding (n is
+// wave-uniform and one of the counts the pipeline produces; any other value
+// waits for everything).
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  switch (n) {
+    case 1: wait_vm<1>(); break;
+    case 10: wait_vm<10>(); break;
+    case 11: wait_vm<11>(); break;
+    case 19: wait_vm<19>(); break;
+    case 29: wait_vm<29>(); break;
+    default: wait_vm<0>(); break;
+  }
 }
 
 __device__ __forceinline__ void pin(int32_t& x) { asm volatile("" : "+v"(x)); }
-
-__device__ __forceinline__ void pin(u32x4_t& x) { asm volatile("" : "+v"(x)); }
 
 // Token row (tile-relative) held by MFMA row m of wave w.  Odd waves use
 // row m ^ 12 so that the transposed LDS reads of two consecutive waves'
 // rows fall in distinct banks.
 __device__ __forceinline__ int tile_row(int w, int m) { return 16 * w + ((w & 1) ? (m ^ 12) : m); }
 
+// Walks the tiles of consecutive requests: request b, tile j of its nt
+// tiles, request range [lo, hi).  Requests without tokens are skipped.  The
+// kv_indptr values come from a 64-entry window held one entry per lane.
+struct TileCursor {
+  int b, j, nt, lo, hi;
+  int win, win_val;
+  __device__ __forceinline__ int tile_lo() const { return lo + (j << TILE_SHIFT); }
+  __device__ __forceinline__ int tile_hi() const { return min(tile_lo() + TILE, hi); }
+};
+
 __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p) {
-  // One row tile, the query of the current request, and the softmax exchange.
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[TILE_BYTES];
-  __shared__ u32x4_t q_lds[2][2 * KCHUNKS][64];  // current query and the next request's
+  // Two row tiles (the one being computed and the next one landing) and the
+  // softmax exchange.
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2 * TILE_BYTES];
   __shared__ float mx_lds[NWAVES][HEADS];
   __shared__ uint2 p_lds[NWAVES][64];
   __shared__ float l_lds[NWAVES][HEADS];
@@ -236,198 +288,182 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   const int seg = item / p.HG;
   const int hg = item - seg * p.HG;
   const int N = p.total_tokens;
-  const int seg_lo = seg * p.seg_len;
-  const int seg_hi = min(N, seg_lo + p.seg_len);
-  if (seg_lo >= seg_hi) return;
-  const int ntiles = (seg_hi - seg_lo + TILE - 1) / TILE;
   const int head = hg * HEADS + t;  // head whose scores / outputs this lane carries
 
-  // ---- loads.  Wave w fetches rows 16w..16w+15 of each tile.  Its 16 x 36
-  // chunks of 16 bytes are numbered P = 36*r + c and lane l takes P = 64j + l
-  // in load j (j < 9): each load instruction reads whole rows back to back
-  // (one contiguous run per row, ~1.8 rows per instruction), the pattern that
-  // gathers random 576-byte rows fastest.  Lanes r < 16 (and their copies at
-  // r + 16k) hold the slot id of row r; each load gets its row's slot with a
-  // cross-lane permute.  A lane whose token lies past the segment reads the
-  // segment's first row instead (a cache hit); its scores and value bytes
-  // are masked out.
+  // ---- this segment's tiles [t0, t0 + ntiles) of the list of all requests'
+  // tiles, and the request holding tile t0 (a scan of per-request tile
+  // counts, 64 requests per step).
+  int t0, ntiles, per_seg, b0 = 0, j0 = 0;
+  {
+    int total = 0;
+    for (int c = 0; c < p.B; c += 64) {
+      const int nt = request_tiles(p.indptr, c + lane, p.B, N);
+      total += wave_sum_i32(nt);
+      // requests without tokens: zero outputs, written by the first segment
+      uint64_t empty = seg == 0 ? __ballot(c + lane < p.B && nt == 0) : 0ull;
+      while (empty) {
+        const int b = c + __builtin_ctzll(empty);
+        empty &= empty - 1;
+        if (hg == 0 && threadIdx.x == 0 && p.req_pieces) p.req_pieces[b] = make_int2(0, 0);
+        for (int i = threadIdx.x; i < HEADS * 64; i += THREADS) {
+          const int h = hg * HEADS + (i >> 6);
+          if (h < p.H)
+            *reinterpret_cast<uint4*>(p.out + ((int64_t)b * p.H + h) * V_WIDTH + 8 * (i & 63)) =
+                make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+    per_seg = max(1, (total + p.nseg - 1) / p.nseg);
+    t0 = seg * per_seg;
+    ntiles = min(total, t0 + per_seg) - t0;
+    if (ntiles <= 0) return;
+    int carry = 0;
+    for (int c = 0; c < p.B; c += 64) {
+      const int nt = request_tiles(p.indptr, c + lane, p.B, N);
+      const int incl = carry + wave_inclusive_scan(nt, lane);
+      const uint64_t hit = __ballot(c + lane < p.B && incl > t0);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        b0 = c + l;
+        j0 = t0 - (__builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(nt, l));
+        break;
+      }
+      carry = __builtin_amdgcn_readlane(incl, 63);
+    }
+  }
+  auto load_window = [&](TileCursor& c, int b) {
+    c.win = b;
+    c.win_val = clamp_tok(p.indptr[min(b + lane, p.B)], N);
+  };
+  // (every field assigned exactly once on every path, so that the cursors
+  // stay in registers)
+  auto set_request = [&](TileCursor& c, int b) {
+    const bool valid = b < p.B;  // past the last request: an empty cursor
+    if (valid && b + 1 - c.win > 63) load_window(c, b);
+    const int lo = __builtin_amdgcn_readlane(c.win_val, valid ? b - c.win : 0);
+    const int hi = max(lo, __builtin_amdgcn_readlane(c.win_val, valid ? b + 1 - c.win : 0));
+    c.b = b;
+    c.lo = valid ? lo : 0;
+    c.hi = valid ? hi : 0;
+    c.nt = valid ? (hi - lo + TILE - 1) >> TILE_SHIFT : 0;
+  };
+  auto advance = [&](TileCursor& c) {
+    if (++c.j < c.nt) return;
+    c.j = 0;
+    do {
+      set_request(c, c.b + 1);
+    } while (c.nt == 0 && c.b < p.B);
+  };
+  TileCursor cc;  // tile being computed
+  load_window(cc, b0);
+  set_request(cc, b0);
+  cc.j = j0;
+  TileCursor lc = cc;  // next tile whose index is loaded
+
+  // ---- row tiles.  Tile k of the segment goes to LDS slot k & 1 by
+  // global->LDS copies, two tiles ahead of use.  Token r of the tile is LDS
+  // row r (592 bytes: the 576-byte row and a 16-byte pad).  Wave w copies
+  // rows 16w..16w+15, a block of 16 x 37 consecutive 16-byte LDS slots: op j
+  // fills slots 64j..64j+63 of it, lane l taking slot P = 64j + l, i.e. row
+  // P / 37, chunk P % 37; pad slots (chunk 36) get a copy of chunk 35 and the
+  // lanes past the block in the last op are masked off.  Each op thus reads
+  // whole rows back to back, the pattern that gathers random 576-byte rows
+  // fastest.  Lanes r < 16 (and their copies at r + 16k) hold the slot id of
+  // row r, which every lane fetches with a cross-lane permute.  Tokens past
+  // the tile's request read the tile's first row (a cache hit of the same
+  // request); their scores are masked out.
   auto opaque_lane = [&]() -> int {  // recomputed per use, not kept across the loop
     int l = lane;
     asm volatile("" : "+v"(l));
     return l;
   };
-  auto load_index = [&](int k) -> int32_t {
-    const int tok = seg_lo + k * TILE + 16 * w + t;
-    return issue_load_i32(p.indices + (tok < seg_hi ? tok : seg_lo));
+  // index of the load cursor's tile, then advance it (past the segment's
+  // last tile the load reads entry 0 and is never used)
+  auto load_next_index = [&]() -> int32_t {
+    const int tlo = lc.tile_lo();
+    const int tok = tlo + 16 * w + t;
+    const int32_t* a = lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) : p.indices;
+    const int32_t v = issue_load_i32(a);
+    advance(lc);
+    return v;
   };
-  auto load_rows = [&](int32_t idx, u32x4_t (&kb)[KCHUNKS]) {
-    const uint8_t* a[KCHUNKS];
+  const uint32_t lds_tiles = (uint32_t)(uintptr_t)(
+      (__attribute__((address_space(3))) uint8_t*)&kv_lds[0]);
+  auto issue_tile = [&](int k, int32_t idx) {
+    const uint32_t base =
+        __builtin_amdgcn_readfirstlane(lds_tiles + (uint32_t)((k & 1) * TILE_BYTES + 16 * w * ROWB));
     const int ln = opaque_lane();
 #pragma unroll
-    for (int j = 0; j < KCHUNKS; ++j) {
+    for (int j = 0; j < DMA_OPS; ++j) {
       const int P = 64 * j + ln;
-      const int r = P / KV_CHUNKS;
-      const int c = P - r * KV_CHUNKS;
-      const uint32_t s = (uint32_t)__shfl(idx, r);
-      a[j] = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
+      const int r = P / ROW_SLOTS;
+      const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
+      const uint32_t s = (uint32_t)__shfl(idx, r & 15);
+      const uint8_t* a = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
+      if (j < DMA_OPS - 1 || P < 16 * ROW_SLOTS) issue_lds_dma16(a, base + 1024 * j);
     }
-    issue_load_rows(kb, a);
   };
-  // stage a tile's rows (this wave's 16) into the LDS row tile
-  auto store_rows = [&](const u32x4_t (&kb)[KCHUNKS]) {
-    const int ln = opaque_lane();
+
+  // ---- query operand (B of the score MFMA), held in registers: for step
+  // s = 2i + e lane (t, g) holds q[head t][64i + 16g + 8e .. +8], the d-order
+  // in which it reads its K row.  Heads >= H read the last head and are
+  // zeroed.
+  auto q_lane_ptr = [&](int b) -> const uint16_t* {
+    return p.q + ((int64_t)b * p.H + min(head, p.H - 1)) * KV_WIDTH + 16 * g;
+  };
+  bf16x8_t qr[QSTEPS];
+  auto finish_q = [&]() {
+    pin_q(qr);
+    if (head >= p.H) {
 #pragma unroll
-    for (int j = 0; j < KCHUNKS; ++j) {
-      const int P = 64 * j + ln;
-      const int r = P / KV_CHUNKS;
-      *reinterpret_cast<u32x4_t*>(kv_lds + (16 * w + r) * ROWB + 16 * (P - r * KV_CHUNKS)) = kb[j];
+      for (int s = 0; s < QSTEPS; ++s) qr[s] = bf16x8_t{};
     }
   };
 
-  u32x4_t kb0[KCHUNKS], kb1[KCHUNKS], kb2[KCHUNKS];
-  int32_t ix0 = load_index(0);
-  int32_t ix1 = load_index(1);
-  int32_t ix2 = load_index(2);
-
-  // ---- first request touching the segment: number of requests ending at or
-  // before seg_lo.  Lane j of a 64-entry window holds kv_indptr[win + j];
-  // for batches up to 63 one load covers the whole array, otherwise a
-  // coarse-then-fine search over kv_indptr[1..B] (64 samples per round) runs
-  // first.  Requests with no tokens are skipped by construction.
-  int cur_b;
-  int win = 0;
-  int win_val;
-  if (p.B <= 63) {
-    win_val = clamp_tok(p.indptr[min(lane, p.B)], N);
-    cur_b = __popcll(__ballot(lane >= 1 && lane <= p.B && win_val <= seg_lo));
-  } else {
-    int lo = 0, n = p.B;
-    while (n > 64) {
-      const int stride = (n + 63) / 64;
-      const int j = lo + lane * stride;
-      const bool le = j < lo + n && clamp_tok(p.indptr[j + 1], N) <= seg_lo;
-      const int c = __popcll(__ballot(le));
-      if (c == 0) { n = 0; break; }
-      const int nlo = lo + (c - 1) * stride + 1;
-      n = min(stride - 1, lo + n - nlo);
-      lo = nlo;
-    }
-    if (n > 0) {
-      const bool le = lane < n && clamp_tok(p.indptr[lo + lane + 1], N) <= seg_lo;
-      lo += __popcll(__ballot(le));
-    }
-    cur_b = __builtin_amdgcn_readfirstlane(lo);
-    win = cur_b;
-    win_val = clamp_tok(p.indptr[min(win + lane, p.B)], N);
-  }
-  auto indptr_at = [&](int b) -> int {
-    if (b - win > 63) {
-      win = b;
-      win_val = clamp_tok(p.indptr[min(win + lane, p.B)], N);
-    }
-    return __builtin_amdgcn_readlane(win_val, b - win);
-  };
-
-  int req_lo = 0, req_hi = 0;
-  if (cur_b < p.B) {
-    req_lo = indptr_at(cur_b);
-    req_hi = indptr_at(cur_b + 1);
-  }
-
-  // ---- query operand (B of the score MFMA), staged once per workgroup in LDS
-  // in operand order: piece c = 64s + l holds, for step s = 2i+e and lane
-  // l = (t, g), q[head t][64i + 16g + 8e .. +8] -- the d-order in which lane
-  // (t, g) reads its K row.  Heads >= H read the last head and are zeroed.
-  auto q_piece_offset = [&](int b, int c) -> int64_t {
-    const int s = c >> 6, l = c & 63;
-    const int h = min(hg * HEADS + (l & 15), p.H - 1);
-    const int d = 64 * (s >> 1) + 16 * (l >> 4) + 8 * (s & 1);
-    return ((int64_t)b * p.H + h) * KV_WIDTH + d;
-  };
-  int qsel = 0;  // which q_lds buffer holds the current query
-  auto store_q_piece = [&](int c, u32x4_t v) {
-    if (hg * HEADS + ((c & 63) & 15) >= p.H) v = u32x4_t{0u, 0u, 0u, 0u};
-    q_lds[qsel][c >> 6][c & 63] = v;
-  };
-
-  wait_vm<0>();
-  pin(ix0);
-  pin(ix1);
-  pin(ix2);
-  // Prologue: only the first request's query (3 pieces per thread) and the
-  // rows of tile 0 are requested before computing starts.  Every workgroup
-  // starts at once; had tiles 1 and 2 been requested too, tile 0 would queue
-  // behind three tiles' worth of traffic from the whole GPU.
+  // Prologue.  The first request's query is copied once into LDS slot 1
+  // (free until tile 1 is requested) and every wave reads its operand from
+  // there: 18 KB through the memory pipeline ahead of tile 0 instead of one
+  // 18 KB copy per wave.  Piece c = 64s + l of the copy holds lane l's
+  // operand for step s.  Issue order: indices of tiles 0 and 1, the query (3
+  // copy ops per wave), rows of tile 0, index of tile 2; once every wave has
+  // read the query, rows of tile 1.
+  int32_t ixE = load_next_index();  // even tiles k: holds the index of tile k + 2
+  int32_t ixO = load_next_index();  // odd tiles
   {
-    u32x4_t q0v[3];
-    const int b0 = min(cur_b, p.B - 1);
+    const uint32_t qbase = lds_tiles + TILE_BYTES;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      const int c = threadIdx.x + j * THREADS < QPIECES ? threadIdx.x + j * THREADS : threadIdx.x;
-      q0v[j] = issue_load_16(p.q + q_piece_offset(b0, c));
+      // ops 0 and 1: pieces 128w + 64j + l; op 2: pieces 1024 + 64(w & 1) + l
+      // (waves of equal parity copy the same bytes to the same place)
+      const int c0 = j < 2 ? 128 * w + 64 * j : 1024 + 64 * (w & 1);
+      const int c = c0 + opaque_lane();
+      const int s = c >> 6, l = c & 63;
+      const int h = min(hg * HEADS + (l & 15), p.H - 1);
+      const int d = 64 * (s >> 1) + 16 * (l >> 4) + 8 * (s & 1);
+      issue_lds_dma16(p.q + ((int64_t)cc.b * p.H + h) * KV_WIDTH + d,
+                      __builtin_amdgcn_readfirstlane(qbase + 16 * c0));
     }
-    load_rows(ix0, kb0);
-    wait_vm<0>();
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      pin(q0v[j]);
-      const int c = threadIdx.x + j * THREADS;
-      if (c < QPIECES) store_q_piece(c, q0v[j]);
-    }
-    pin(kb0);
-    store_rows(kb0);
   }
-  int q_b = cur_b;
+  wait_vm<3>();  // indices of tiles 0 and 1 landed
+  pin(ixE);
+  pin(ixO);
+  issue_tile(0, ixE);
+  ixE = load_next_index();
+  wait_vm<1 + DMA_OPS>();  // query landed (younger: rows of tile 0, index of tile 2)
   __syncthreads();
-  // Then, in the main loop's order ("index of j+1 before rows of j"): index of
-  // tile 3, rows of tiles 1 and 2.
-  ix0 = load_index(3);
-  load_rows(ix1, kb1);
-  load_rows(ix2, kb2);
-  // Request switch inside the segment: reload the query (compiler-managed
-  // loads).  Every wave has passed the barriers of the previous piece, so no
-  // one still reads the old query.
-  auto load_q = [&](int b) {
-    for (int c = threadIdx.x; c < QPIECES; c += THREADS) store_q_piece(c, *reinterpret_cast<const u32x4_t*>(p.q + q_piece_offset(b, c)));
-    __syncthreads();
-    q_b = b;
-  };
-  // Next request's query, copied into the idle q_lds buffer one tile ahead
-  // of the switch.  Called at a tile's top between the index load and the row
-  // loads: the next tile's "at most 10 outstanding" wait then proves the copy
-  // landed, since it sits between two operations that wait already covers.
-  // Heads >= H get the last head's values (their outputs are never written).
-  int pref_b = -1;
-  auto maybe_prefetch_q = [&](int k) {
-    if (pref_b >= 0 || cur_b + 1 >= p.B) return;
-    const int nlo = seg_lo + (k + 1) * TILE;
-    const int nhi = min(nlo + TILE, seg_hi);
-    if (req_hi < nlo || req_hi >= nhi) return;  // the switch is not in tile k+1
-    const int nb = cur_b + 1;
-    if (indptr_at(nb + 1) <= req_hi) return;  // next request empty: slow path
-    const uint32_t qbase = (uint32_t)(uintptr_t)(
-        (__attribute__((address_space(3))) u32x4_t*)&q_lds[qsel ^ 1][0][0]);
+  {
+    const u32x4_t* qs = reinterpret_cast<const u32x4_t*>(kv_lds + TILE_BYTES);
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      if (j < 2 || w < 2) {  // 1152 pieces = 2 x 512 + 128
-        const int c = THREADS * j + 64 * w + lane;
-        issue_lds_dma16(p.q + q_piece_offset(nb, c),
-                        __builtin_amdgcn_readfirstlane(qbase + 16 * (THREADS * j + 64 * w)));
-      }
+    for (int s = 0; s < QSTEPS; ++s) qr[s] = __builtin_bit_cast(bf16x8_t, qs[64 * s + lane]);
+    if (head >= p.H) {
+#pragma unroll
+      for (int s = 0; s < QSTEPS; ++s) qr[s] = bf16x8_t{};
     }
-    pref_b = nb;
-  };
-  auto switch_q = [&](int b) {
-    if (pref_b == b) {  // every wave's copy has landed (see maybe_prefetch_q)
-      __syncthreads();
-      qsel ^= 1;
-      q_b = b;
-    } else {
-      load_q(b);
-    }
-    pref_b = -1;
-  };
-
+  }
+  __syncthreads();  // every wave holds its query: slot 1 may be refilled
+  if (ntiles > 1) issue_tile(1, ixO);
+  wait_vm_upto(ntiles > 1 ? 1 + DMA_OPS : 1);  // rows of tile 0 landed
+  __syncthreads();
 
   // ---- LDS read offsets.  Score operand: lane (t, g) reads chunk 4i + g
   // (bytes 64i + 16g .. +16) of MFMA row t, i.e. tile row tile_row(w, t).
@@ -448,46 +484,118 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   for (int c = 0; c < 4; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   float l_w = 0.f;
-  i32x2_t vt[4][4];  // value operand of the current tile, read once per tile
+  bool whole_request = j0 == 0;  // the current request's first tile is in this segment
+  // Pieces of a request: the segments its tiles [first, first + nt) fall in.
+  // Recorded for the combine by the workgroup holding the request's first
+  // tile (head group 0).
+  auto record_pieces = [&](int first_tile) {
+    if (hg == 0 && threadIdx.x == 0) {
+      const int s0 = first_tile / per_seg;
+      p.req_pieces[cc.b] = make_int2(s0, (first_tile + cc.nt - 1) / per_seg - s0 + 1);
+    }
+  };
+  if (whole_request) record_pieces(t0);
 
-  // One piece (the part of a tile that belongs to one request).  When
-  // `next` is non-null this is the tile's last piece: after the max exchange
-  // (every wave is past its reads of the row tile) the next tile's rows are
-  // staged, and the probability exchange barrier publishes them.
-  auto run_piece = [&](int tile_lo, int plo, int phi, u32x4_t* next) {
-    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* kp = kv_lds + k_off;
+  auto finish_request = [&](bool complete) {
+    const float lsum = wave_sum_over_groups(l_w);
+    if (g == 0) l_lds[w][t] = lsum;
+    __syncthreads();
+    float l = 0.f;
 #pragma unroll
-    for (int i = 0; i < KCHUNKS; ++i) {
+    for (int v = 0; v < NWAVES; ++v) l += l_lds[v][t];
+    if (complete) {
+      if (head < p.H) {
+        const float inv = p.kv_scale / l;
+        uint16_t* op = p.out + ((int64_t)cc.b * p.H + head) * V_WIDTH + 64 * w + 4 * g;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          uint2 v;
+          v.x = pack_bf16x2(O[c][0] * inv, O[c][1] * inv);
+          v.y = pack_bf16x2(O[c][2] * inv, O[c][3] * inv);
+          *reinterpret_cast<uint2*>(op + 16 * c) = v;
+        }
+      }
+    } else {
+      const int64_t piece = (int64_t)(seg + cc.b) * p.Hp + head;
+      const float inv = 1.0f / l;
+      float* op = p.part_o + piece * V_WIDTH + 64 * w + 4 * g;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<float4*>(op + 16 * c) =
+            make_float4(O[c][0] * inv, O[c][1] * inv, O[c][2] * inv, O[c][3] * inv);
+      if (w == 0 && g == 0) p.part_lse[piece] = m_run + __builtin_amdgcn_logf(l);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    l_w = 0.f;
+    m_run = -INFINITY;
+  };
+
+  // Tile k: its rows are in slot k & 1 (published by the previous barrier);
+  // ix_cur holds the index of tile k+2 and ix_next receives that of tile k+3.
+  //   scores -> [barrier: maxima] -> loads for later tiles -> probabilities
+  //   -> wait for tile k+1's rows -> [barrier: probabilities, tile k+1]
+  //   -> P.V -> (request end: output)
+  // After the first barrier every wave is past its reads of slot k & 1, so
+  // the rows of tile k+2 may be copied into it.
+  bool q_pending = false;  // the query of this tile's request is in flight
+  auto process_tile = [&](int k, int32_t& ix_cur, int32_t& ix_next) {
+    const int tile_lo = cc.tile_lo();
+    const int tile_hi = cc.tile_hi();
+    const bool last_of_request = cc.j + 1 == cc.nt;
+    const uint8_t* slot = kv_lds + (k & 1) * TILE_BYTES;
+    if (q_pending) {  // issued before the rows of tile k+1: those may stay in flight
+      wait_vm_upto(k + 1 < ntiles ? DMA_OPS : 0);
+      finish_q();
+      q_pending = false;
+    }
+
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* kp = slot + k_off;
+#pragma unroll
+    for (int i = 0; i < KSTEPS; ++i) {
       const u32x4_t kv = *reinterpret_cast<const u32x4_t*>(kp + 64 * i);
-      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv[0], kv[1]),
-                                                   __builtin_bit_cast(bf16x8_t, q_lds[qsel][2 * i][lane]),
-                                                   a0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv[2], kv[3]),
-                                                   __builtin_bit_cast(bf16x8_t, q_lds[qsel][2 * i + 1][lane]),
-                                                   a1, 0, 0, 0);
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv[0], kv[1]), qr[2 * i], a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv[2], kv[3]), qr[2 * i + 1], a1, 0, 0, 0);
+    }
+    // value operand, read before the barrier after which the slot is refilled
+    i32x2_t vt[4][4];
+    {
+      const uint8_t* vbase = slot + tr_off;
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          vt[st][c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2_t*)(vbase + 32 * ROWB * st + 16 * c));
     }
     float s[4];
     float lmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int tok = tile_lo + s_tok0 + r;
-      const bool ok = tok >= plo && tok < phi;
+      const bool ok = tile_lo + s_tok0 + r < tile_hi;
       s[r] = ok ? (a0[r] + a1[r]) * p.score_scale : -INFINITY;
       lmax = fmaxf(lmax, s[r]);
     }
     lmax = wave_max_over_groups(lmax);
     if (g == 0) mx_lds[w][t] = lmax;
     __syncthreads();
-    if (next) {
-      // The next tile's rows were issued before 19 or more younger operations
-      // (tile 0: rows of tiles 2 and 3 and an index; later tiles: two tiles'
-      // rows and indices), so "at most 19 outstanding" proves they arrived.
-      u32x4_t (&nk)[KCHUNKS] = *reinterpret_cast<u32x4_t(*)[KCHUNKS]>(next);
-      wait_vm<19>();
-      pin(nk);
-      store_rows(nk);
+
+    // Loads for later tiles: index of tile k+3; the query of tile k+1 if it
+    // starts a new request (qr is dead until then); rows of tile k+2.  The
+    // index of tile k+2 was issued before the rows of tile k+1, so "at most
+    // DMA_OPS outstanding" proves it arrived without waiting for those rows.
+    wait_vm_upto(k + 1 < ntiles ? DMA_OPS : 0);
+    pin(ix_cur);
+    ix_next = load_next_index();
+    const bool new_q = last_of_request && k + 1 < ntiles;
+    TileCursor nc = cc;
+    if (new_q) {
+      advance(nc);
+      issue_load_q(qr, q_lane_ptr(nc.b));
     }
+    if (k + 2 < ntiles) issue_tile(k + 2, ix_cur);
+
     float tmax = mx_lds[0][t];
 #pragma unroll
     for (int v = 1; v < NWAVES; ++v) tmax = fmaxf(tmax, mx_lds[v][t]);
@@ -507,6 +615,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     l_w += (bf16_bits_to_f32(p01 & 0xFFFFu) + bf16_bits_to_f32(p01 >> 16)) +
            (bf16_bits_to_f32(p23 & 0xFFFFu) + bf16_bits_to_f32(p23 >> 16));
     p_lds[w][lane] = make_uint2(p01, p23);
+    // rows of tile k+1 landed (younger: index k+3, maybe a query, rows k+2)
+    if (k + 1 < ntiles) wait_vm_upto(1 + (new_q ? QSTEPS : 0) + (k + 2 < ntiles ? DMA_OPS : 0));
     __syncthreads();
 
     bf16x8_t pb[4];
@@ -517,217 +627,58 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       u32x4_t v = {x.x, x.y, y.x, y.y};
       pb[st] = __builtin_bit_cast(bf16x8_t, v);
     }
-    // Rows of the tile outside this piece (another request, or past the
-    // segment) have probability 0; their value bytes are zeroed as well so
-    // that a NaN in another request's rows cannot enter through 0 * NaN.
-    const bool mask_v = plo > tile_lo || phi < tile_lo + TILE;
+    // Rows past the request's end in a partial tile are copies of the tile's
+    // first row with probability 0, so their value bytes need no masking.
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      uint32_t mlo = 0xFFFFFFFFu, mhi = 0xFFFFFFFFu;
-      if (mask_v) {
-        // bytes jj < 4: tokens 32st + 4g + jj; bytes jj >= 4: 32st + 16 + 4(g^3) + jj - 4
-        mlo = run_mask(tile_lo + 32 * st + 4 * g, plo, phi);
-        mhi = run_mask(tile_lo + 32 * st + 16 + 4 * (g ^ 3), plo, phi);
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t lo = (uint32_t)vt[st][c].x & mlo;
-        const uint32_t hi = (uint32_t)vt[st][c].y & mhi;
-        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(lo, hi), pb[st], O[c], 0, 0, 0);
-      }
-    }
-  };
-
-  auto finish_piece = [&](bool complete) {
-    const float lsum = wave_sum_over_groups(l_w);
-    if (g == 0) l_lds[w][t] = lsum;
-    __syncthreads();
-    float l = 0.f;
-#pragma unroll
-    for (int v = 0; v < NWAVES; ++v) l += l_lds[v][t];
-    if (complete) {
-      if (head < p.H) {
-        const float inv = p.kv_scale / l;
-        uint16_t* op = p.out + ((int64_t)cur_b * p.H + head) * V_WIDTH + 64 * w + 4 * g;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint2 v;
-          v.x = pack_bf16x2(O[c][0] * inv, O[c][1] * inv);
-          v.y = pack_bf16x2(O[c][2] * inv, O[c][3] * inv);
-          *reinterpret_cast<uint2*>(op + 16 * c) = v;
-        }
-      }
-    } else {
-      const int64_t piece = (int64_t)(seg + cur_b) * p.Hp + head;
-      const float inv = 1.0f / l;
-      float* op = p.part_o + piece * V_WIDTH + 64 * w + 4 * g;
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<float4*>(op + 16 * c) =
-            make_float4(O[c][0] * inv, O[c][1] * inv, O[c][2] * inv, O[c][3] * inv);
-      if (w == 0 && g == 0) p.part_lse[piece] = m_run + __builtin_amdgcn_logf(l);
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    l_w = 0.f;
-    m_run = -INFINITY;
-  };
+        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            e4m3x8_to_bf16x8((uint32_t)vt[st][c].x, (uint32_t)vt[st][c].y), pb[st], O[c], 0, 0, 0);
 
-  // Tile k: its rows are in the LDS tile (published by the previous
-  // barrier); `next` holds the rows of tile k+1 in registers (they have
-  // arrived) and is staged during the tile's last piece.
-  auto process_tile = [&](int k, u32x4_t (&next)[KCHUNKS]) {
-    const int tile_lo = seg_lo + k * TILE;
-    const int tile_hi = min(tile_lo + TILE, seg_hi);
-    {
-      const uint8_t* vbase = kv_lds + tr_off;
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          vt[st][c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) i32x2_t*)(vbase + 32 * ROWB * st + 16 * c));
-    }
-    int pos = tile_lo;
-    bool staged = false;
-    while (pos < tile_hi) {
-      while (req_hi <= pos && cur_b < p.B) {
-        ++cur_b;
-        req_lo = req_hi;
-        req_hi = cur_b < p.B ? max(req_lo, indptr_at(cur_b + 1)) : req_lo;
-      }
-      if (cur_b >= p.B) break;  // malformed kv_indptr: tokens past the last request
-      const int plo = pos;
-      const int phi = min(tile_hi, req_hi);
-      if (q_b != cur_b) switch_q(cur_b);
-      const bool last = phi == tile_hi;
-      run_piece(tile_lo, plo, phi, last ? &next[0] : nullptr);
-      staged |= last;
-      if (phi == req_hi || phi == seg_hi) finish_piece(req_lo >= seg_lo && req_hi <= seg_hi);
-      pos = phi;
-    }
-    if (!staged) {  // no piece reached the tile end (malformed kv_indptr): keep the barrier count
-      __syncthreads();
-      wait_vm<19>();
-      pin(next);
-      store_rows(next);
-      __syncthreads();
+    if (last_of_request || k + 1 == ntiles) finish_request(whole_request && last_of_request);
+    if (new_q) {
+      cc = nc;
+      whole_request = true;
+      record_pieces(t0 + k + 1);
+      q_pending = true;
+    } else {
+      advance(cc);
     }
   };
 
-  // ---- main loop: a three-slot register ring.  At tile k the rows of tile
-  // k+1 wait in registers to be staged into LDS (after arriving), and the
-  // rows of tiles k+2 and k+3 are in flight.  Issue order per tile: index of
-  // tile k+4, then the rows of tile k+3 once the index of k+3 has arrived --
-  // "at most 10 outstanding" (rows of k+2, index of k+4) proves it, and also
-  // proves the rows of k+1 arrived.  Tile 0 is peeled: there the index of
-  // tile 3 precedes the rows of tiles 1 and 2, so 19 may stay outstanding.
-  // Ring slots: rows of tile j live in kb[j % 3]; indices of tile j in ix[j % 3].
-  ix1 = load_index(4);
-  wait_vm<19>();
-  pin(ix0);
-  maybe_prefetch_q(0);
-  load_rows(ix0, kb0);
-  process_tile(0, kb1);
-  for (int k = 0; k < ntiles; k += 3) {
-    if (k > 0) {
-      ix1 = load_index(k + 4);
-      wait_vm<10>();
-      pin(ix0);
-      pin(kb1);
-      maybe_prefetch_q(k);
-      load_rows(ix0, kb0);
-      process_tile(k, kb1);
-    }
+  // ---- main loop, unrolled by two so that each index register keeps one
+  // role: at even tiles ixE holds the index of tile k+2 and ixO receives
+  // that of tile k+3; at odd tiles the other way round.
+  for (int k = 0; k < ntiles; k += 2) {
+    process_tile(k, ixE, ixO);
     if (k + 1 >= ntiles) break;
-    ix2 = load_index(k + 5);
-    wait_vm<10>();
-    pin(ix1);
-    pin(kb2);
-    maybe_prefetch_q(k + 1);
-    load_rows(ix1, kb1);
-    process_tile(k + 1, kb2);
-    if (k + 2 >= ntiles) break;
-    ix0 = load_index(k + 6);
-    wait_vm<10>();
-    pin(ix2);
-    pin(kb0);
-    maybe_prefetch_q(k + 2);
-    load_rows(ix2, kb2);
-    process_tile(k + 2, kb0);
+    process_tile(k + 1, ixO, ixE);
   }
-  wait_vm<0>();  // retire prefetches issued past the last tile
+  wait_vm<0>();  // retire index loads issued past the last tile
 }
 
-// One wave per (request, head): merges the partials of a request that spans
-// several segments.  out = scale * sum_s w_s o_s / sum_s w_s with
-// w_s = 2^(lse_s - max lse).  Requests with no tokens get zeros; requests
-// inside one segment were written by the split kernel.  The log-sum-exps of
-// up to 64 pieces are loaded in one wave-wide step and the partial outputs
-// four pieces at a time, so a request costs one or two memory latencies, not
-// one per piece.
+struct CombineParams {
+  const int2* req_pieces;
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* out;
+  int32_t H;
+  int32_t Hp;
+  float kv_scale;
+};
+
+// One wave per (request, head): merges the pieces of a request that spans
+// several segments.  Requests without tokens and requests inside one segment
+// were written by the split kernel.
 __global__ __launch_bounds__(256) void mla_combine_kernel(const CombineParams p) {
   const int b = blockIdx.x;
   const int head = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
   if (head >= p.H) return;
-  const int N = p.total_tokens;
-  const int lo = clamp_tok(p.indptr[b], N);
-  const int hi = max(lo, clamp_tok(p.indptr[b + 1], N));
-  uint16_t* op = p.out + ((int64_t)b * p.H + head) * V_WIDTH + 8 * lane;
-  if (hi <= lo) {
-    *reinterpret_cast<uint4*>(op) = make_uint4(0u, 0u, 0u, 0u);
-    return;
-  }
-  const int s0 = lo / p.seg_len;
-  const int s1 = (hi - 1) / p.seg_len;
-  if (s0 == s1) return;
-  const int np = s1 - s0 + 1;
-  const float* lse = p.part_lse + (int64_t)(s0 + b) * p.Hp + head;  // piece i at lse[i * Hp]
-  float M = -INFINITY;
-  for (int i = lane; i < np; i += 64) M = fmaxf(M, lse[(int64_t)i * p.Hp]);
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  const float* po = p.part_o + ((int64_t)(s0 + b) * p.Hp + head) * V_WIDTH + 8 * lane;
-  const int64_t pstride = (int64_t)p.Hp * V_WIDTH;  // floats between consecutive pieces
-  for (int base = 0; base < np; base += 64) {
-    const int cnt = min(64, np - base);
-    const float wl = lane < cnt ? __builtin_amdgcn_exp2f(lse[(int64_t)(base + lane) * p.Hp] - M) : 0.f;
-    int i = 0;
-    for (; i + 4 <= cnt; i += 4) {
-      float4 x[4], y[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4* q = reinterpret_cast<const float4*>(po + (int64_t)(base + i + u) * pstride);
-        x[u] = q[0];
-        y[u] = q[1];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wgt =
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i + u));
-        acc[0] += wgt * x[u].x; acc[1] += wgt * x[u].y; acc[2] += wgt * x[u].z; acc[3] += wgt * x[u].w;
-        acc[4] += wgt * y[u].x; acc[5] += wgt * y[u].y; acc[6] += wgt * y[u].z; acc[7] += wgt * y[u].w;
-        den += wgt;
-      }
-    }
-    for (; i < cnt; ++i) {
-      const float4* q = reinterpret_cast<const float4*>(po + (int64_t)(base + i) * pstride);
-      const float4 x = q[0], y = q[1];
-      const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), i));
-      acc[0] += wgt * x.x; acc[1] += wgt * x.y; acc[2] += wgt * x.z; acc[3] += wgt * x.w;
-      acc[4] += wgt * y.x; acc[5] += wgt * y.y; acc[6] += wgt * y.z; acc[7] += wgt * y.w;
-      den += wgt;
-    }
-  }
-  const float inv = p.kv_scale / den;
-  uint4 v;
-  v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-  v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-  *reinterpret_cast<uint4*>(op) = v;
+  const int2 rp = p.req_pieces[b];
+  if (rp.y <= 1) return;
+  merge_pieces(p.part_o, p.part_lse, p.Hp, b, rp.x, rp.y, head, p.kv_scale,
+               p.out + ((int64_t)b * p.H + head) * V_WIDTH, threadIdx.x & 63);
 }
 
 }  // namespace
@@ -736,16 +687,16 @@ DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_token
   DecodePlan pl{};
   pl.HG = (num_heads + HEADS - 1) / HEADS;
   pl.Hp = pl.HG * HEADS;
-  if (total_tokens <= 0) return pl;
-  // one 8-wave workgroup per compute unit in flight; head groups of a segment
-  // are separate workgroups that share the segment's rows through L2
-  int64_t nseg_target = num_cus / pl.HG;
-  if (nseg_target < 1) nseg_target = 1;
-  // Segments need no alignment (tiles are counted from each segment's start),
-  // so the token stream is cut into exactly nseg_target pieces when it can be.
-  const int64_t seg = (total_tokens + nseg_target - 1) / nseg_target;
-  pl.seg_len = (int32_t)seg;
-  pl.nseg = (int32_t)((total_tokens + seg - 1) / seg);
+  // One 8-wave workgroup per compute unit in flight; head groups of a
+  // segment are separate workgroups that share the segment's rows through
+  // L2.  The tile list has at most ceil(N / 128) + batch tiles, so more
+  // segments than that would stay empty.
+  int64_t nseg = num_cus / pl.HG;
+  if (nseg < 1) nseg = 1;
+  const int64_t max_tiles = (total_tokens > 0 ? (total_tokens + TILE - 1) / TILE : 0) + batch;
+  if (nseg > max_tiles) nseg = max_tiles;
+  if (nseg < 1) nseg = 1;
+  pl.nseg = (int32_t)nseg;
   pl.items = pl.nseg * pl.HG;
   if (pl.HG > 1) {
     pl.xcd_per = (pl.items + 7) / 8;
@@ -754,10 +705,15 @@ DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_token
     pl.xcd_per = pl.items;
     pl.grid = pl.items;
   }
+  // Workspace: per-request piece ranges, then partial outputs and
+  // log2-sum-exps; pieces are indexed segment + request, fewer than
+  // nseg + batch.
   const size_t npieces = (size_t)pl.nseg + (size_t)batch;
+  const size_t ranges_bytes = (size_t)batch * 2 * sizeof(int32_t);
   const size_t o_bytes = npieces * pl.Hp * V_WIDTH * sizeof(float);
   const size_t lse_bytes = npieces * pl.Hp * sizeof(float);
-  pl.lse_offset = (o_bytes + 255) / 256 * 256;
+  pl.part_o_offset = (ranges_bytes + 255) / 256 * 256;
+  pl.lse_offset = pl.part_o_offset + (o_bytes + 255) / 256 * 256;
   pl.workspace_bytes = pl.lse_offset + (lse_bytes + 255) / 256 * 256;
   return pl;
 }
@@ -767,42 +723,37 @@ hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t 
                              int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
                              float sm_scale, uint16_t* out, void* workspace, const DecodePlan& pl,
                              hipStream_t stream) {
-  float* part_o = reinterpret_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + pl.lse_offset);
-  if (total_tokens > 0) {
-    SplitParams sp;
-    sp.q = q;
-    sp.pool = kv_pool;
-    sp.indptr = kv_indptr;
-    sp.indices = kv_indices;
-    sp.out = out;
-    sp.part_o = part_o;
-    sp.part_lse = part_lse;
-    sp.max_slot = (uint32_t)(num_slots - 1);
-    sp.total_tokens = (int32_t)total_tokens;
-    sp.B = batch;
-    sp.H = num_heads;
-    sp.HG = pl.HG;
-    sp.Hp = pl.Hp;
-    sp.seg_len = pl.seg_len;
-    sp.items = pl.items;
-    sp.xcd_per = pl.xcd_per;
-    sp.score_scale = (float)((double)sm_scale * (double)scale * 1.4426950408889634);
-    sp.kv_scale = scale;
-    hipLaunchKernelGGL(mla_split_kernel, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  char* ws = reinterpret_cast<char*>(workspace);
+  SplitParams sp;
+  sp.q = q;
+  sp.pool = kv_pool;
+  sp.indptr = kv_indptr;
+  sp.indices = kv_indices;
+  sp.out = out;
+  sp.part_o = reinterpret_cast<float*>(ws + pl.part_o_offset);
+  sp.part_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
+  sp.req_pieces = total_tokens > 0 ? reinterpret_cast<int2*>(ws) : nullptr;
+  sp.max_slot = num_slots > 0 ? (uint32_t)(num_slots - 1) : 0u;
+  sp.total_tokens = (int32_t)total_tokens;
+  sp.B = batch;
+  sp.H = num_heads;
+  sp.HG = pl.HG;
+  sp.Hp = pl.Hp;
+  sp.nseg = pl.nseg;
+  sp.items = pl.items;
+  sp.xcd_per = pl.xcd_per;
+  sp.score_scale = (float)((double)sm_scale * (double)scale * 1.4426950408889634);
+  sp.kv_scale = scale;
+  hipLaunchKernelGGL(mla_split_kernel, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || total_tokens == 0) return e;  // no tokens: nothing to merge
   CombineParams cp;
-  cp.indptr = kv_indptr;
-  cp.part_o = part_o;
-  cp.part_lse = part_lse;
+  cp.req_pieces = reinterpret_cast<const int2*>(ws);
+  cp.part_o = sp.part_o;
+  cp.part_lse = sp.part_lse;
   cp.out = out;
-  cp.total_tokens = (int32_t)total_tokens;
-  cp.B = batch;
   cp.H = num_heads;
   cp.Hp = pl.Hp;
-  cp.seg_len = pl.seg_len > 0 ? pl.seg_len : 1;
   cp.kv_scale = scale;
   hipLaunchKernelGGL(mla_combine_kernel, dim3(batch, (num_heads + 3) / 4), dim3(256), 0, stream, cp);
   return hipGetLastError();

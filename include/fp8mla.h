@@ -110,13 +110,16 @@ int gather_cast_fp8_bf16(const uint8_t* pool, int64_t num_slots, const int32_t* 
  *   out         uint16 [batch, num_heads, 512]  BF16 output, written
  *   workspace   device scratch of at least mla_decode_fp8_workspace_bytes(...)
  *               bytes, owned by the caller; contents need no initialisation and
- *               are garbage afterwards.  Two calls in flight at once on
- *               different streams need different workspaces.
+ *               are garbage afterwards.  Calls that may overlap (different
+ *               streams) need different workspaces.  May be NULL when
+ *               total_tokens == 0.
  *   1 <= batch, 1 <= num_heads <= FP8MLA_MAX_HEADS, total_tokens >= 0,
  *   num_slots >= 1 (unless total_tokens == 0).
- * Work is split into equal token segments over all compute units
- * (flash-decoding split-K) and merged by a second kernel; the host never
- * reads kv_indptr, so the call stays asynchronous.
+ * Each request's tokens are cut into 128-token tiles; the list of all tiles
+ * is split into equal segments over the compute units (flash-decoding
+ * split-K), and a second kernel merges the pieces of requests that span
+ * several segments.  The host never reads kv_indptr, so the call stays
+ * asynchronous.
  */
 int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
                    const int32_t* kv_indptr, const int32_t* kv_indices, int64_t total_tokens,
@@ -125,8 +128,9 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
 
 /*
  * Workspace size in bytes for mla_decode_fp8 on the CURRENT device with these
- * sizes.  Returns 0 for invalid sizes.  Host-only except for one query of
- * the device's compute-unit count (cached per device).
+ * sizes (0 when total_tokens == 0: no workspace is needed).  Returns 0 for
+ * invalid sizes.  Host-only except for one query of the device's
+ * compute-unit count (cached per device).
  */
 size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens);
 

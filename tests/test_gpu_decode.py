@@ -103,6 +103,22 @@ def test_deterministic(dev):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+def test_workspace_reuse_across_shapes(dev):
+    # One workspace, filled with garbage first, reused by calls of different
+    # shapes: the workspace is pure scratch, every call must match the oracle.
+    shapes = [(3, 32, [3000, 50, 9000]), (5, 16, [700, 1, 0, 2049, 130]), (2, 17, [4000, 4000])]
+    need = max(fm.mla_decode_fp8_workspace_bytes(len(L), H, sum(L), dev) for _, H, L in shapes)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=dev)
+    for rep in range(2):
+        for i, (B, H, L) in enumerate(shapes):
+            w = workloads.small(B, H, L, seed=100 + i, device=dev)
+            out = fm.mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale,
+                                    workspace=ws)
+            torch.cuda.synchronize()
+            ref = oracle.mla_decode_ref(*oracle_args(w))
+            assert_attention_close(out, ref, "reuse %d/%d" % (rep, i))
+
+
 def test_slot_relocation_invariance(dev):
     w = workloads.small(2, 16, [400, 300], seed=9, device=dev)
     a = _run(w)
