@@ -170,7 +170,7 @@ __device__ __forceinline__ void merge_pieces(const float* part_o, const float* p
   *reinterpret_cast<uint4*>(op + 8 * lane) = v;
 }
 
-// ---- explicitly pipelined loads.  Index, query and row loads are issued as
+// ---- explicitly pipelined loads.  Index, query and row copies are issued as
 // inline assembly and waited for with an explicit s_waitcnt vmcnt(N): left to
 // itself the compiler sinks prefetches down to their first use or drains
 // every load at a barrier, which removes the overlap the pipeline exists
@@ -183,43 +183,6 @@ __device__ __forceinline__ int32_t issue_load_i32(const int32_t* p) {
   int32_t v;
   asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p));
   return v;
-}
-
-// Query operand of one lane: 9 pairs of 16-byte pieces 64 elements (128
-// bytes) apart.
-__device__ __forceinline__ void issue_load_q(bf16x8_t (&q)[QSTEPS], const uint16_t* qp) {
-  asm volatile(
-      "global_load_dwordx4 %0, %18, off\n\t"
-      "global_load_dwordx4 %1, %18, off offset:16\n\t"
-      "global_load_dwordx4 %2, %18, off offset:128\n\t"
-      "global_load_dwordx4 %3, %18, off offset:144\n\t"
-      "global_load_dwordx4 %4, %18, off offset:256\n\t"
-      "global_load_dwordx4 %5, %18, off offset:272\n\t"
-      "global_load_dwordx4 %6, %18, off offset:384\n\t"
-      "global_load_dwordx4 %7, %18, off offset:400\n\t"
-      "global_load_dwordx4 %8, %18, off offset:512\n\t"
-      "global_load_dwordx4 %9, %18, off offset:528\n\t"
-      "global_load_dwordx4 %10, %18, off offset:640\n\t"
-      "global_load_dwordx4 %11, %18, off offset:656\n\t"
-      "global_load_dwordx4 %12, %18, off offset:768\n\t"
-      "global_load_dwordx4 %13, %18, off offset:784\n\t"
-      "global_load_dwordx4 %14, %18, off offset:896\n\t"
-      "global_load_dwordx4 %15, %18, off offset:912\n\t"
-      "global_load_dwordx4 %16, %18, off offset:1024\n\t"
-      "global_load_dwordx4 %17, %18, off offset:1040"
-      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]),
-        "=&v"(q[7]), "=&v"(q[8]), "=&v"(q[9]), "=&v"(q[10]), "=&v"(q[11]), "=&v"(q[12]),
-        "=&v"(q[13]), "=&v"(q[14]), "=&v"(q[15]), "=&v"(q[16]), "=&v"(q[17])
-      : "v"(qp));
-}
-
-__device__ __forceinline__ void pin_q(bf16x8_t (&q)[QSTEPS]) {
-  asm volatile(""
-               : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]),
-                 "+v"(q[6]), "+v"(q[7]), "+v"(q[8]));
-  asm volatile(""
-               : "+v"(q[9]), "+v"(q[10]), "+v"(q[11]), "+v"(q[12]), "+v"(q[13]), "+v"(q[14]),
-                 "+v"(q[15]), "+v"(q[16]), "+v"(q[17]));
 }
 
 // Global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
@@ -246,8 +209,6 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
     case 1: wait_vm<1>(); break;
     case 10: wait_vm<10>(); break;
     case 11: wait_vm<11>(); break;
-    case 19: wait_vm<19>(); break;
-    case 29: wait_vm<29>(); break;
     default: wait_vm<0>(); break;
   }
 }
@@ -406,33 +367,17 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
 
   // ---- query operand (B of the score MFMA), held in registers: for step
   // s = 2i + e lane (t, g) holds q[head t][64i + 16g + 8e .. +8], the d-order
-  // in which it reads its K row.  Heads >= H read the last head and are
-  // zeroed.
-  auto q_lane_ptr = [&](int b) -> const uint16_t* {
-    return p.q + ((int64_t)b * p.H + min(head, p.H - 1)) * KV_WIDTH + 16 * g;
-  };
-  bf16x8_t qr[QSTEPS];
-  auto finish_q = [&]() {
-    pin_q(qr);
-    if (head >= p.H) {
+  // in which it reads its K row.  A request's query is copied once per
+  // workgroup into 18 KB of an LDS row slot (3 copy ops per wave; piece
+  // c = 64s + l holds lane l's operand for step s) and every wave reads its
+  // operand from there: one 18 KB copy through the memory pipeline instead of
+  // one per wave.  Heads >= H copy the last head and are zeroed.
+  constexpr int QCOPY_OPS = 3;
+  constexpr int QCOPY_BYTES = QSTEPS * 64 * 16;  // 18432: rows 0..31 of a slot
+  static_assert(QCOPY_BYTES <= 32 * ROWB, "query copy must fit in waves 0-1's rows");
+  auto issue_query_copy = [&](int b, uint32_t lds_base) {
 #pragma unroll
-      for (int s = 0; s < QSTEPS; ++s) qr[s] = bf16x8_t{};
-    }
-  };
-
-  // Prologue.  The first request's query is copied once into LDS slot 1
-  // (free until tile 1 is requested) and every wave reads its operand from
-  // there: 18 KB through the memory pipeline ahead of tile 0 instead of one
-  // 18 KB copy per wave.  Piece c = 64s + l of the copy holds lane l's
-  // operand for step s.  Issue order: indices of tiles 0 and 1, the query (3
-  // copy ops per wave), rows of tile 0, index of tile 2; once every wave has
-  // read the query, rows of tile 1.
-  int32_t ixE = load_next_index();  // even tiles k: holds the index of tile k + 2
-  int32_t ixO = load_next_index();  // odd tiles
-  {
-    const uint32_t qbase = lds_tiles + TILE_BYTES;
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
+    for (int j = 0; j < QCOPY_OPS; ++j) {
       // ops 0 and 1: pieces 128w + 64j + l; op 2: pieces 1024 + 64(w & 1) + l
       // (waves of equal parity copy the same bytes to the same place)
       const int c0 = j < 2 ? 128 * w + 64 * j : 1024 + 64 * (w & 1);
@@ -440,26 +385,36 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       const int s = c >> 6, l = c & 63;
       const int h = min(hg * HEADS + (l & 15), p.H - 1);
       const int d = 64 * (s >> 1) + 16 * (l >> 4) + 8 * (s & 1);
-      issue_lds_dma16(p.q + ((int64_t)cc.b * p.H + h) * KV_WIDTH + d,
-                      __builtin_amdgcn_readfirstlane(qbase + 16 * c0));
+      issue_lds_dma16(p.q + ((int64_t)b * p.H + h) * KV_WIDTH + d,
+                      __builtin_amdgcn_readfirstlane(lds_base + 16 * c0));
     }
-  }
-  wait_vm<3>();  // indices of tiles 0 and 1 landed
-  pin(ixE);
-  pin(ixO);
-  issue_tile(0, ixE);
-  ixE = load_next_index();
-  wait_vm<1 + DMA_OPS>();  // query landed (younger: rows of tile 0, index of tile 2)
-  __syncthreads();
-  {
-    const u32x4_t* qs = reinterpret_cast<const u32x4_t*>(kv_lds + TILE_BYTES);
+  };
+  bf16x8_t qr[QSTEPS];
+  auto read_query = [&](const uint8_t* lds_q) {
+    const u32x4_t* qs = reinterpret_cast<const u32x4_t*>(lds_q);
 #pragma unroll
     for (int s = 0; s < QSTEPS; ++s) qr[s] = __builtin_bit_cast(bf16x8_t, qs[64 * s + lane]);
     if (head >= p.H) {
 #pragma unroll
       for (int s = 0; s < QSTEPS; ++s) qr[s] = bf16x8_t{};
     }
-  }
+  };
+
+  // Prologue.  The first request's query goes through LDS slot 1 (free until
+  // tile 1 is requested).  Issue order: indices of tiles 0 and 1, the query,
+  // rows of tile 0, index of tile 2; once every wave has read the query, rows
+  // of tile 1.
+  int32_t ixE = load_next_index();  // even tiles k: holds the index of tile k + 2
+  int32_t ixO = load_next_index();  // odd tiles
+  issue_query_copy(cc.b, lds_tiles + TILE_BYTES);
+  wait_vm<QCOPY_OPS>();  // indices of tiles 0 and 1 landed
+  pin(ixE);
+  pin(ixO);
+  issue_tile(0, ixE);
+  ixE = load_next_index();
+  wait_vm<1 + DMA_OPS>();  // query landed (younger: rows of tile 0, index of tile 2)
+  __syncthreads();
+  read_query(kv_lds + TILE_BYTES);
   __syncthreads();  // every wave holds its query: slot 1 may be refilled
   if (ntiles > 1) issue_tile(1, ixO);
   wait_vm_upto(ntiles > 1 ? 1 + DMA_OPS : 1);  // rows of tile 0 landed
@@ -538,17 +493,11 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   //   -> P.V -> (request end: output)
   // After the first barrier every wave is past its reads of slot k & 1, so
   // the rows of tile k+2 may be copied into it.
-  bool q_pending = false;  // the query of this tile's request is in flight
   auto process_tile = [&](int k, int32_t& ix_cur, int32_t& ix_next) {
     const int tile_lo = cc.tile_lo();
     const int tile_hi = cc.tile_hi();
     const bool last_of_request = cc.j + 1 == cc.nt;
     const uint8_t* slot = kv_lds + (k & 1) * TILE_BYTES;
-    if (q_pending) {  // issued before the rows of tile k+1: those may stay in flight
-      wait_vm_upto(k + 1 < ntiles ? DMA_OPS : 0);
-      finish_q();
-      q_pending = false;
-    }
 
     f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
     const uint8_t* kp = slot + k_off;
@@ -581,20 +530,24 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     if (g == 0) mx_lds[w][t] = lmax;
     __syncthreads();
 
-    // Loads for later tiles: index of tile k+3; the query of tile k+1 if it
-    // starts a new request (qr is dead until then); rows of tile k+2.  The
-    // index of tile k+2 was issued before the rows of tile k+1, so "at most
-    // DMA_OPS outstanding" proves it arrived without waiting for those rows.
+    // Loads for later tiles: index of tile k+3, rows of tile k+2 into this
+    // slot.  The index of tile k+2 was issued before the rows of tile k+1, so
+    // "at most DMA_OPS outstanding" proves it arrived without waiting for
+    // those rows.  When tile k+1 starts a new request, its query is copied
+    // into rows 0..31 of this slot first, and waves 0 and 1 (the owners of
+    // those rows) copy their rows of tile k+2 only after every wave has read
+    // the query (after the next barrier).
     wait_vm_upto(k + 1 < ntiles ? DMA_OPS : 0);
     pin(ix_cur);
     ix_next = load_next_index();
     const bool new_q = last_of_request && k + 1 < ntiles;
+    const bool rows_now = k + 2 < ntiles && (!new_q || w >= 2);
     TileCursor nc = cc;
     if (new_q) {
       advance(nc);
-      issue_load_q(qr, q_lane_ptr(nc.b));
+      issue_query_copy(nc.b, lds_tiles + (uint32_t)((k & 1) * TILE_BYTES));
     }
-    if (k + 2 < ntiles) issue_tile(k + 2, ix_cur);
+    if (rows_now) issue_tile(k + 2, ix_cur);
 
     float tmax = mx_lds[0][t];
 #pragma unroll
@@ -615,9 +568,15 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     l_w += (bf16_bits_to_f32(p01 & 0xFFFFu) + bf16_bits_to_f32(p01 >> 16)) +
            (bf16_bits_to_f32(p23 & 0xFFFFu) + bf16_bits_to_f32(p23 >> 16));
     p_lds[w][lane] = make_uint2(p01, p23);
-    // rows of tile k+1 landed (younger: index k+3, maybe a query, rows k+2)
-    if (k + 1 < ntiles) wait_vm_upto(1 + (new_q ? QSTEPS : 0) + (k + 2 < ntiles ? DMA_OPS : 0));
+    // rows of tile k+1 (and a new query) landed; younger: index of k+3 unless
+    // a query was copied after it, and rows of k+2 if issued
+    if (k + 1 < ntiles) wait_vm_upto((new_q ? 0 : 1) + (rows_now ? DMA_OPS : 0));
     __syncthreads();
+    if (new_q) {
+      read_query(slot);
+      __syncthreads();  // every wave holds the new query: rows 0..31 may be refilled
+      if (w < 2 && k + 2 < ntiles) issue_tile(k + 2, ix_cur);
+    }
 
     bf16x8_t pb[4];
 #pragma unroll
@@ -641,7 +600,6 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       cc = nc;
       whole_request = true;
       record_pieces(t0 + k + 1);
-      q_pending = true;
     } else {
       advance(cc);
     }
