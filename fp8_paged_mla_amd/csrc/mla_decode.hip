@@ -15,7 +15,7 @@
 // segments are balanced by tiles, not by request, so long and short requests
 // cost the same per token.  For every request it touches a workgroup writes
 // either the final output (request entirely inside the segment) or a partial
-// (o normalised, log2-sum-exp) that the combine kernel merges.
+// (o normalised, fp16, and its log2-sum-exp) that the combine kernel merges.
 //
 // Inside a workgroup (8 waves, 16 heads), per tile:
 //  * the tile's 128 rows are copied global -> LDS by the waves themselves
@@ -53,6 +53,8 @@ constexpr int KSTEPS = KV_WIDTH / 64;             // 16-byte K reads per lane pe
 constexpr int QSTEPS = 2 * KSTEPS;                // 18 MFMA steps of 32 dims over 576
 constexpr int DMA_OPS = (16 * ROW_SLOTS + 63) / 64;  // LDS-copy ops per wave per tile: 10
 static_assert(TILE == 1 << TILE_SHIFT, "tile size");
+constexpr int TILE_W = 4;   // segment balancing: weight of a tile
+constexpr int START_W = 2;  // extra weight of a request's first tile
 
 struct SplitParams {
   const uint16_t* q;
@@ -60,7 +62,7 @@ struct SplitParams {
   const int32_t* indptr;
   const int32_t* indices;
   uint16_t* out;
-  float* part_o;
+  uint16_t* part_o;  // fp16 bits
   float* part_lse;
   int2* req_pieces;  // per request: (segment of its first piece, number of pieces)
   uint32_t max_slot;
@@ -122,24 +124,34 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 // all their loads issued together (one memory latency per eight pieces) and
 // folded in with a running maximum.  Lane l produces output columns
 // 8l .. 8l+7.
-__device__ __forceinline__ void merge_pieces(const float* part_o, const float* part_lse, int Hp,
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+
+// Partial outputs are stored as fp16 (round to nearest even), in E4M3 units
+// (before the per-tensor scale): every partial is a convex combination of
+// E4M3 values, |o| <= 448, so fp16 cannot overflow, and its 11-bit
+// significand is finer than the bf16 the merged output is rounded to.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w).x; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w).y; }
+
+__device__ __forceinline__ void merge_pieces(const uint16_t* part_o, const float* part_lse, int Hp,
                                              int b, int s0, int np, int head, float kv_scale,
                                              uint16_t* op, int lane) {
   const float* lse = part_lse + (int64_t)(s0 + b) * Hp + head;  // piece i at lse[i * Hp]
-  const float* po = part_o + ((int64_t)(s0 + b) * Hp + head) * V_WIDTH + 8 * lane;
-  const int64_t pstride = (int64_t)Hp * V_WIDTH;  // floats between consecutive pieces
+  const uint16_t* po = part_o + ((int64_t)(s0 + b) * Hp + head) * V_WIDTH + 8 * lane;
+  const int64_t pstride = (int64_t)Hp * V_WIDTH;  // elements between consecutive pieces
   float M = -INFINITY, den = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < np; base += 8) {
     const int cnt = min(8, np - base);
     const float lv = lane < cnt ? lse[(int64_t)(base + lane) * Hp] : -INFINITY;
-    float4 x[8], y[8];
+    uint4 x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {  // u >= cnt re-reads the last piece (in bounds, unused)
-      const float4* q = reinterpret_cast<const float4*>(po + (int64_t)(base + min(u, cnt - 1)) * pstride);
-      x[u] = q[0];
-      y[u] = q[1];
-    }
+    for (int u = 0; u < 8; ++u)  // u >= cnt re-reads the last piece (in bounds, unused)
+      x[u] = *reinterpret_cast<const uint4*>(po + (int64_t)(base + min(u, cnt - 1)) * pstride);
     float cm = lv;
 #pragma unroll
     for (int off = 1; off < 8; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
@@ -155,8 +167,10 @@ __device__ __forceinline__ void merge_pieces(const float* part_o, const float* p
     for (int u = 0; u < 8; ++u) {
       if (u < cnt) {
         const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
-        acc[0] += wgt * x[u].x; acc[1] += wgt * x[u].y; acc[2] += wgt * x[u].z; acc[3] += wgt * x[u].w;
-        acc[4] += wgt * y[u].x; acc[5] += wgt * y[u].y; acc[6] += wgt * y[u].z; acc[7] += wgt * y[u].w;
+        acc[0] += wgt * f16_lo(x[u].x); acc[1] += wgt * f16_hi(x[u].x);
+        acc[2] += wgt * f16_lo(x[u].y); acc[3] += wgt * f16_hi(x[u].y);
+        acc[4] += wgt * f16_lo(x[u].z); acc[5] += wgt * f16_hi(x[u].z);
+        acc[6] += wgt * f16_lo(x[u].w); acc[7] += wgt * f16_hi(x[u].w);
         den += wgt;
       }
     }
@@ -251,47 +265,77 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   const int N = p.total_tokens;
   const int head = hg * HEADS + t;  // head whose scores / outputs this lane carries
 
-  // ---- this segment's tiles [t0, t0 + ntiles) of the list of all requests'
-  // tiles, and the request holding tile t0 (a scan of per-request tile
-  // counts, 64 requests per step).
-  int t0, ntiles, per_seg, b0 = 0, j0 = 0;
-  {
-    int total = 0;
-    for (int c = 0; c < p.B; c += 64) {
-      const int nt = request_tiles(p.indptr, c + lane, p.B, N);
-      total += wave_sum_i32(nt);
-      // requests without tokens: zero outputs, written by the first segment
-      uint64_t empty = seg == 0 ? __ballot(c + lane < p.B && nt == 0) : 0ull;
-      while (empty) {
-        const int b = c + __builtin_ctzll(empty);
-        empty &= empty - 1;
-        if (hg == 0 && threadIdx.x == 0 && p.req_pieces) p.req_pieces[b] = make_int2(0, 0);
-        for (int i = threadIdx.x; i < HEADS * 64; i += THREADS) {
-          const int h = hg * HEADS + (i >> 6);
-          if (h < p.H)
-            *reinterpret_cast<uint4*>(p.out + ((int64_t)b * p.H + h) * V_WIDTH + 8 * (i & 63)) =
-                make_uint4(0u, 0u, 0u, 0u);
-        }
+  // ---- this segment's tiles.  Tiles are weighted by their cost: TILE_W per
+  // tile and START_W more for the first tile of a request (the query switch
+  // and the extra output).  Request b's tile j sits at weighted position
+  // x = P_b + START_W + TILE_W * j, P_b being the total weight of the
+  // requests before b; segment s takes the tiles with x in
+  // [ceil(s W / nseg), ceil((s+1) W / nseg)), W the total weight, so tile x
+  // belongs to segment floor(x nseg / W).  Found with two wave-wide scans
+  // over the requests, 64 per step: the global index t0 of the first tile,
+  // its request b0 and tile j0, and the number of tiles.
+  // (Weights fit in int: W <= 4 * (N / 128 + B) + 2 * B.)
+  int W = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    const int nt = request_tiles(p.indptr, c + lane, p.B, N);
+    W += wave_sum_i32(nt > 0 ? TILE_W * nt + START_W : 0);
+    // requests without tokens: zero outputs, written by the first segment
+    uint64_t empty = seg == 0 ? __ballot(c + lane < p.B && nt == 0) : 0ull;
+    while (empty) {
+      const int b = c + __builtin_ctzll(empty);
+      empty &= empty - 1;
+      if (hg == 0 && threadIdx.x == 0 && p.req_pieces) p.req_pieces[b] = make_int2(0, 0);
+      for (int i = threadIdx.x; i < HEADS * 64; i += THREADS) {
+        const int h = hg * HEADS + (i >> 6);
+        if (h < p.H)
+          *reinterpret_cast<uint4*>(p.out + ((int64_t)b * p.H + h) * V_WIDTH + 8 * (i & 63)) =
+              make_uint4(0u, 0u, 0u, 0u);
       }
-    }
-    per_seg = max(1, (total + p.nseg - 1) / p.nseg);
-    t0 = seg * per_seg;
-    ntiles = min(total, t0 + per_seg) - t0;
-    if (ntiles <= 0) return;
-    int carry = 0;
-    for (int c = 0; c < p.B; c += 64) {
-      const int nt = request_tiles(p.indptr, c + lane, p.B, N);
-      const int incl = carry + wave_inclusive_scan(nt, lane);
-      const uint64_t hit = __ballot(c + lane < p.B && incl > t0);
-      if (hit) {
-        const int l = __builtin_ctzll(hit);
-        b0 = c + l;
-        j0 = t0 - (__builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(nt, l));
-        break;
-      }
-      carry = __builtin_amdgcn_readlane(incl, 63);
     }
   }
+  // Consecutive tile positions are at most TILE_W + START_W apart, so with
+  // segments at least that wide every segment holds a tile and the pieces of
+  // a request are consecutive segments; later workgroups stay idle.
+  const int nseg = min(p.nseg, W / (TILE_W + START_W));
+  if (seg >= nseg) return;
+  const int x_lo = (int)(((int64_t)seg * W + nseg - 1) / nseg);
+  const int x_hi = (int)(((int64_t)(seg + 1) * W + nseg - 1) / nseg);
+  auto segment_of = [&](int x) -> int { return (int)((int64_t)x * nseg / W); };
+  // global index t0 of the first tile at or after x_lo (its request b0, tile
+  // j0, weight P0 before b0) and t1 of the first at or after x_hi
+  int t0 = -1, t1 = -1, b0 = 0, j0 = 0, P0 = 0;
+  {
+    int wcarry = 0, tcarry = 0;
+    for (int c = 0; c < p.B && t1 < 0; c += 64) {
+      const int nt = request_tiles(p.indptr, c + lane, p.B, N);
+      const int w = nt > 0 ? TILE_W * nt + START_W : 0;
+      const int Pb = wcarry + wave_inclusive_scan(w, lane) - w;
+      const int TB = tcarry + wave_inclusive_scan(nt, lane) - nt;
+      const int last_x = Pb + START_W + TILE_W * (nt - 1);
+      auto first_at = [&](int X, int& t, bool keep) {
+        const uint64_t hit = __ballot(nt > 0 && last_x >= X);
+        if (t >= 0 || !hit) return;
+        const int l = __builtin_ctzll(hit);
+        const int pb = __builtin_amdgcn_readlane(Pb, l);
+        const int rel = X - pb - START_W;
+        const int j = rel <= 0 ? 0 : (rel + TILE_W - 1) / TILE_W;
+        t = __builtin_amdgcn_readlane(TB, l) + j;
+        if (keep) {
+          b0 = c + l;
+          j0 = j;
+          P0 = pb;
+        }
+      };
+      first_at(x_lo, t0, true);
+      first_at(x_hi, t1, false);
+      wcarry += wave_sum_i32(w);
+      tcarry += wave_sum_i32(nt);
+      if (c + 64 >= p.B && t1 < 0) t1 = tcarry;  // past the last tile
+    }
+  }
+  if (t0 < 0) return;
+  const int ntiles = t1 - t0;
+  if (ntiles <= 0) return;
   auto load_window = [&](TileCursor& c, int b) {
     c.win = b;
     c.win_val = clamp_tok(p.indptr[min(b + lane, p.B)], N);
@@ -440,16 +484,18 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   float m_run = -INFINITY;
   float l_w = 0.f;
   bool whole_request = j0 == 0;  // the current request's first tile is in this segment
+  int P_cur = P0;                 // weight of the requests before the current one
   // Pieces of a request: the segments its tiles [first, first + nt) fall in.
   // Recorded for the combine by the workgroup holding the request's first
   // tile (head group 0).
-  auto record_pieces = [&](int first_tile) {
+  auto record_pieces = [&]() {
     if (hg == 0 && threadIdx.x == 0) {
-      const int s0 = first_tile / per_seg;
-      p.req_pieces[cc.b] = make_int2(s0, (first_tile + cc.nt - 1) / per_seg - s0 + 1);
+      const int s0 = segment_of(P_cur + START_W);
+      const int s1 = segment_of(P_cur + START_W + TILE_W * (cc.nt - 1));
+      p.req_pieces[cc.b] = make_int2(s0, s1 - s0 + 1);
     }
   };
-  if (whole_request) record_pieces(t0);
+  if (whole_request) record_pieces();
 
   auto finish_request = [&](bool complete) {
     const float lsum = wave_sum_over_groups(l_w);
@@ -473,11 +519,11 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     } else {
       const int64_t piece = (int64_t)(seg + cc.b) * p.Hp + head;
       const float inv = 1.0f / l;
-      float* op = p.part_o + piece * V_WIDTH + 64 * w + 4 * g;
+      uint16_t* op = p.part_o + piece * V_WIDTH + 64 * w + 4 * g;
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<float4*>(op + 16 * c) =
-            make_float4(O[c][0] * inv, O[c][1] * inv, O[c][2] * inv, O[c][3] * inv);
+        *reinterpret_cast<uint2*>(op + 16 * c) =
+            make_uint2(pack_f16x2(O[c][0] * inv, O[c][1] * inv), pack_f16x2(O[c][2] * inv, O[c][3] * inv));
       if (w == 0 && g == 0) p.part_lse[piece] = m_run + __builtin_amdgcn_logf(l);
     }
 #pragma unroll
@@ -597,9 +643,10 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
 
     if (last_of_request || k + 1 == ntiles) finish_request(whole_request && last_of_request);
     if (new_q) {
+      P_cur += TILE_W * cc.nt + START_W;
       cc = nc;
       whole_request = true;
-      record_pieces(t0 + k + 1);
+      record_pieces();
     } else {
       advance(cc);
     }
@@ -618,7 +665,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
 
 struct CombineParams {
   const int2* req_pieces;
-  const float* part_o;
+  const uint16_t* part_o;
   const float* part_lse;
   uint16_t* out;
   int32_t H;
@@ -668,7 +715,7 @@ DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_token
   // nseg + batch.
   const size_t npieces = (size_t)pl.nseg + (size_t)batch;
   const size_t ranges_bytes = (size_t)batch * 2 * sizeof(int32_t);
-  const size_t o_bytes = npieces * pl.Hp * V_WIDTH * sizeof(float);
+  const size_t o_bytes = npieces * pl.Hp * V_WIDTH * sizeof(uint16_t);
   const size_t lse_bytes = npieces * pl.Hp * sizeof(float);
   pl.part_o_offset = (ranges_bytes + 255) / 256 * 256;
   pl.lse_offset = pl.part_o_offset + (o_bytes + 255) / 256 * 256;
@@ -688,7 +735,7 @@ hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t 
   sp.indptr = kv_indptr;
   sp.indices = kv_indices;
   sp.out = out;
-  sp.part_o = reinterpret_cast<float*>(ws + pl.part_o_offset);
+  sp.part_o = reinterpret_cast<uint16_t*>(ws + pl.part_o_offset);
   sp.part_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
   sp.req_pieces = total_tokens > 0 ? reinterpret_cast<int2*>(ws) : nullptr;
   sp.max_slot = num_slots > 0 ? (uint32_t)(num_slots - 1) : 0u;
