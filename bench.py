@@ -72,9 +72,10 @@ def read_traffic(launch_units):
         return None
 
 
-def cpu_baseline(w, budget_s=20.0):
-    """The float64 oracle on the host: requests of the same workload, one by
-    one, until about budget_s seconds have run (at least one request)."""
+def cpu_baseline(w, budget_s=15.0):
+    """The float64 oracle on the host over the same workload: its requests one
+    by one, in repeated passes over the batch, until about budget_s seconds
+    have run (at least one full pass)."""
     import numpy as np
     import oracle
     try:
@@ -87,17 +88,16 @@ def cpu_baseline(w, budget_s=20.0):
             w.scale, w.sm_scale)
     ctx = threadpool_limits(limits=cores) if threadpool_limits else None
     tokens = 0
-    done = 0
+    passes = 0
     t0 = time.perf_counter()
     try:
         if ctx:
             ctx.__enter__()
-        for b in range(w.B):
-            oracle.mla_decode_ref(*args, requests=[b])
-            tokens += int(w.lengths[b])
-            done += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
+        while passes == 0 or time.perf_counter() - t0 < budget_s:
+            for b in range(w.B):
+                oracle.mla_decode_ref(*args, requests=[b])
+                tokens += int(w.lengths[b])
+            passes += 1
     finally:
         if ctx:
             ctx.__exit__(None, None, None)
@@ -107,8 +107,9 @@ def cpu_baseline(w, budget_s=20.0):
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": "float64 numpy oracle over %d of %d requests (%d tokens, %.1f s) of the same "
-                  "batch-40 workload, replica 0" % (done, w.B, tokens, dt),
+        "sample": "float64 numpy oracle (BLAS on up to %d threads), %d passes over the %d "
+                  "requests (%d tokens each pass) of the batch-40 workload's replica 0: %d "
+                  "tokens in %.1f s" % (cores, passes, w.B, tokens // max(passes, 1), tokens, dt),
     }
 
 
@@ -217,7 +218,7 @@ def main():
             "unit": "GB/s",
             "frac": round(mean_useful / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic": read_traffic(1),
-            "kernel": "mla_split_kernel + mla_combine_kernel (one mla_decode_fp8 call)",
+            "kernel": "one mla_decode_fp8 call: mla_split_kernel + mla_combine_kernel",
             "algorithmic_bytes_per_call": int(mean_useful),
         },
     }
