@@ -232,10 +232,11 @@ def main():
 
 def cast_path_step(fm, workloads, torch, dev, args):
     """The pages' per-step comparison over `layers` distinct 495,552-slot FP8
-    pools (one request, 4,096 tokens, 64 heads): full-pool cast, gather-cast of
-    the active slots, and the fused decode, each summed over the layers.  The
-    BF16 attention that follows a cast on the pages is not included; the
-    numbers are the cast kernels' own time."""
+    pools (one request, 4,096 tokens, 64 heads), each summed over the layers:
+    the cast kernels alone (full-pool cast, gather-cast of the active slots),
+    the two complete fallback paths (cast + BF16-row attention with the
+    original indices; gather-cast + BF16-row attention over indices 0..n-1),
+    and the fused FP8 decode."""
     L = args.layers
     w0 = workloads.config(3, 0, device=dev)
     pools = [w0.pool] + [workloads.random_pool(495552, seed=3000 + 7 * l + 1, device=dev)
@@ -246,6 +247,19 @@ def cast_path_step(fm, workloads, torch, dev, args):
     out = torch.empty((w0.B, w0.H, 512), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(256, fm.mla_decode_fp8_workspace_bytes(w0.B, w0.H, w0.total_tokens)),
                      dtype=torch.uint8, device=dev)
+    ws16 = torch.empty(max(256, fm.mla_decode_bf16_workspace_bytes(w0.B, w0.H, w0.total_tokens)),
+                       dtype=torch.uint8, device=dev)
+    seq = torch.arange(w0.total_tokens, dtype=torch.int32, device=dev)
+
+    def cast_path(p):
+        fm.cast_pool_fp8_bf16(p, out=cast_out)
+        fm.mla_decode_bf16(w0.q, cast_out, w0.indptr, w0.indices, w0.scale, w0.sm_scale,
+                           out=out, workspace=ws16)
+
+    def gather_path(p):
+        fm.gather_cast_fp8_bf16(p, w0.indices, out=g_out)
+        fm.mla_decode_bf16(w0.q, g_out, w0.indptr, seq, w0.scale, w0.sm_scale, out=out,
+                           workspace=ws16)
 
     def timed(fn, reps=3):
         best = None
@@ -267,6 +281,8 @@ def cast_path_step(fm, workloads, torch, dev, args):
     gather_ms = timed(lambda p: fm.gather_cast_fp8_bf16(p, w0.indices, out=g_out))
     fused_ms = timed(lambda p: fm.mla_decode_fp8(w0.q, p, w0.indptr, w0.indices, w0.scale,
                                                  w0.sm_scale, out=out, workspace=ws))
+    cast_path_ms = timed(cast_path)
+    gather_path_ms = timed(gather_path)
     cast_bytes = 495552 * 576 * 3
     gather_bytes = w0.total_tokens * (4 + 576 + 1152)
     return {
@@ -284,6 +300,11 @@ def cast_path_step(fm, workloads, torch, dev, args):
         "gather_cast_us_per_layer": round(gather_ms * 1e3 / L, 2),
         "fused_decode_ms_per_step": round(fused_ms, 4),
         "fused_decode_us_per_layer": round(fused_ms * 1e3 / L, 2),
+        "cast_then_attend_ms_per_step": round(cast_path_ms, 3),
+        "gather_then_attend_ms_per_step": round(gather_path_ms, 4),
+        "gather_then_attend_us_per_layer": round(gather_path_ms * 1e3 / L, 2),
+        "fused_speedup_vs_cast_then_attend": round(cast_path_ms / fused_ms, 1),
+        "fused_speedup_vs_gather_then_attend": round(gather_path_ms / fused_ms, 2),
     }
 
 

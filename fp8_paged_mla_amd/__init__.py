@@ -31,6 +31,8 @@ __all__ = [
     "gather_cast_fp8_bf16",
     "mla_decode_fp8",
     "mla_decode_fp8_workspace_bytes",
+    "mla_decode_bf16",
+    "mla_decode_bf16_workspace_bytes",
     "status_string",
     "KV_WIDTH",
     "V_WIDTH",
@@ -65,6 +67,10 @@ def library() -> ctypes.CDLL:
     lib.mla_decode_fp8.restype = ctypes.c_int
     lib.mla_decode_fp8_workspace_bytes.argtypes = [i32, i32, i64]
     lib.mla_decode_fp8_workspace_bytes.restype = sz
+    lib.mla_decode_bf16.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, f32, f32, vp, vp, sz, vp]
+    lib.mla_decode_bf16.restype = ctypes.c_int
+    lib.mla_decode_bf16_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.mla_decode_bf16_workspace_bytes.restype = sz
     lib.fp8mla_status_string.argtypes = [ctypes.c_int]
     lib.fp8mla_status_string.restype = ctypes.c_char_p
     lib.fp8mla_abi_version.argtypes = []
@@ -204,4 +210,56 @@ def mla_decode_fp8(q: torch.Tensor, kv_pool: torch.Tensor, kv_indptr: torch.Tens
                                   float(scale), float(sm_scale), out.data_ptr(),
                                   workspace.data_ptr(), ws_bytes, _stream_handle(dev)),
                "mla_decode_fp8")
+    return out
+
+
+def mla_decode_bf16_workspace_bytes(batch: int, num_heads: int, total_tokens: int,
+                                    device=None) -> int:
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        return int(library().mla_decode_bf16_workspace_bytes(int(batch), int(num_heads),
+                                                             int(total_tokens)))
+
+
+def mla_decode_bf16(q: torch.Tensor, kv: torch.Tensor, kv_indptr: torch.Tensor,
+                    kv_indices: torch.Tensor, scale: float, sm_scale: float,
+                    out: torch.Tensor = None, workspace: torch.Tensor = None) -> torch.Tensor:
+    """The same decode over BF16 latent rows (benchmark-only: the attention of
+    the cast-then-attend fallback paths).
+
+    q [B, H, 576] bf16; kv [num_rows, 576] bf16 (e.g. a cast pool or a
+    gathered buffer); kv_indptr [B+1] int32; kv_indices int32 row ids.
+    """
+    if kv.dim() == 3 and kv.shape[1] == 1:
+        kv = kv.view(kv.shape[0], kv.shape[2])
+    _require(q, "q", torch.bfloat16)
+    dev = q.device
+    _require(kv, "kv", torch.bfloat16, dev)
+    _require(kv_indptr, "kv_indptr", torch.int32, dev)
+    _require(kv_indices, "kv_indices", torch.int32, dev)
+    if kv.dim() != 2 or kv.shape[1] != KV_WIDTH:
+        raise ValueError("kv must be [num_rows, 576], got %s" % (tuple(kv.shape),))
+    if q.dim() != 3 or q.shape[2] != KV_WIDTH:
+        raise ValueError("q must be [B, H, 576], got %s" % (tuple(q.shape),))
+    B, H = q.shape[0], q.shape[1]
+    if kv_indptr.dim() != 1 or kv_indptr.shape[0] != B + 1:
+        raise ValueError("kv_indptr must be [B+1]")
+    if kv_indices.dim() != 1:
+        raise ValueError("kv_indices must be 1-D")
+    total = kv_indices.shape[0]
+    if out is None:
+        out = torch.empty((B, H, V_WIDTH), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev)
+    if tuple(out.shape) != (B, H, V_WIDTH):
+        raise ValueError("out must be [%d, %d, 512]" % (B, H))
+    lib = library()
+    with torch.cuda.device(dev):
+        need = int(lib.mla_decode_bf16_workspace_bytes(B, H, total))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        _require(workspace, "workspace", torch.uint8, dev)
+        _check(lib.mla_decode_bf16(q.data_ptr(), kv.data_ptr(), kv.shape[0], kv_indptr.data_ptr(),
+                                   kv_indices.data_ptr(), total, B, H, float(scale), float(sm_scale),
+                                   out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                   _stream_handle(dev)), "mla_decode_bf16")
     return out

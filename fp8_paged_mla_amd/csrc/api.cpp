@@ -88,7 +88,8 @@ size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t 
   if (total_tokens == 0) return 0;
   const int cus = current_device_cus();
   if (cus <= 0) return 0;
-  return fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus).workspace_bytes;
+  return fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::kFp8TileTokens)
+      .workspace_bytes;
 }
 
 int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
@@ -107,12 +108,50 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
     return FP8MLA_ERR_MISALIGNED;
   const int cus = current_device_cus();
   if (cus <= 0) return FP8MLA_ERR_HIP;
-  const fp8mla::DecodePlan plan = fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus);
+  const fp8mla::DecodePlan plan =
+      fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::kFp8TileTokens);
   if (total_tokens > 0 && workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
   const hipError_t e = fp8mla::launch_mla_decode(q, kv_pool, num_slots, kv_indptr, kv_indices,
                                                  total_tokens, batch, num_heads, scale, sm_scale,
                                                  out, workspace, plan,
                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
+}
+
+size_t mla_decode_bf16_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens) {
+  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_tokens < 0 ||
+      total_tokens > kMaxTokens)
+    return 0;
+  if (total_tokens == 0) return 0;
+  const int cus = current_device_cus();
+  if (cus <= 0) return 0;
+  return fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::kBf16TileTokens)
+      .workspace_bytes;
+}
+
+int mla_decode_bf16(const uint16_t* q, const uint16_t* kv, int64_t num_rows,
+                    const int32_t* kv_indptr, const int32_t* kv_indices, int64_t total_tokens,
+                    int32_t batch, int32_t num_heads, float scale, float sm_scale, uint16_t* out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_tokens < 0 ||
+      total_tokens > kMaxTokens || num_rows < 0 || num_rows > kMaxSlots)
+    return FP8MLA_ERR_BAD_SHAPE;
+  if (total_tokens > 0 && num_rows == 0) return FP8MLA_ERR_BAD_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.0f) || !isfinite(sm_scale)) return FP8MLA_ERR_BAD_SCALAR;
+  if (!q || !kv_indptr || !out) return FP8MLA_ERR_NULL_PTR;
+  if (total_tokens > 0 && (!kv || !kv_indices || !workspace)) return FP8MLA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(out) || !aligned4(kv_indptr)) return FP8MLA_ERR_MISALIGNED;
+  if (total_tokens > 0 && (!aligned16(kv) || !aligned4(kv_indices) || !aligned16(workspace)))
+    return FP8MLA_ERR_MISALIGNED;
+  const int cus = current_device_cus();
+  if (cus <= 0) return FP8MLA_ERR_HIP;
+  const fp8mla::DecodePlan plan =
+      fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::kBf16TileTokens);
+  if (total_tokens > 0 && workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
+  const hipError_t e = fp8mla::launch_mla_decode_bf16(q, kv, num_rows, kv_indptr, kv_indices,
+                                                      total_tokens, batch, num_heads, scale,
+                                                      sm_scale, out, workspace, plan,
+                                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
 }
 

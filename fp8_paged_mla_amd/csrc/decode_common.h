@@ -1,0 +1,308 @@
+// Pieces shared by the split-K MLA decode kernels (FP8 and BF16 KV rows) of
+// libfp8mla.so: the work split over request tiles, the tile cursor, the
+// explicitly pipelined memory operations and the merge of partial results.
+#pragma once
+
+#include "device_common.h"
+
+#include <math.h>
+
+namespace fp8mla {
+namespace decode {
+
+constexpr int HEADS = 16;   // query heads per workgroup (the MFMA N dimension)
+constexpr int TILE_W = 4;   // segment balancing: weight of a tile
+constexpr int START_W = 2;  // extra weight of a request's first tile
+
+struct SplitParams {
+  const uint16_t* q;
+  const uint8_t* pool;      // KV rows (E4M3FN bytes or BF16 bits)
+  const int32_t* indptr;
+  const int32_t* indices;
+  uint16_t* out;
+  uint16_t* part_o;         // fp16 bits
+  float* part_lse;
+  int2* req_pieces;         // per request: (segment of its first piece, number of pieces)
+  uint32_t max_slot;
+  int32_t total_tokens;
+  int32_t B;
+  int32_t H;
+  int32_t HG;
+  int32_t Hp;
+  int32_t nseg;     // segments the tile list is cut into (at most)
+  int32_t items;    // nseg * HG
+  int32_t xcd_per;
+  float score_scale;  // sm_scale * scale * log2(e): scores in the base-2 domain
+  float kv_scale;
+};
+
+__device__ __forceinline__ float wave_max_over_groups(float x) {
+  // lanes h, h+16, h+32, h+48 hold the same head
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_over_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ int clamp_tok(int v, int n) { return v < 0 ? 0 : (v > n ? n : v); }
+
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// ---- request tiles.  Request b covers tokens [lo_b, hi_b) with
+// lo_b = clamp(kv_indptr[b], 0, N) and hi_b = max(lo_b, clamp(kv_indptr[b+1],
+// 0, N)), and has ceil((hi_b - lo_b) / 2^SHIFT) tiles.
+template <int SHIFT>
+__device__ __forceinline__ int request_tiles(const int32_t* indptr, int b, int B, int N) {
+  if (b >= B) return 0;
+  const int lo = clamp_tok(indptr[b], N);
+  const int hi = max(lo, clamp_tok(indptr[b + 1], N));
+  return (hi - lo + (1 << SHIFT) - 1) >> SHIFT;
+}
+
+// ---- the work split.  Tiles are weighted by their cost: TILE_W per tile and
+// START_W more for the first tile of a request (the query switch and the
+// extra output).  Request b's tile j sits at weighted position
+// x = P_b + START_W + TILE_W * j, P_b being the total weight of the requests
+// before b; segment s takes the tiles with x in [ceil(s W / n), ceil((s+1) W
+// / n)), W the total weight, so tile x belongs to segment floor(x n / W).
+// Consecutive tile positions are at most TILE_W + START_W apart, so with at
+// most W / (TILE_W + START_W) segments every segment holds a tile and the
+// pieces of a request are consecutive segments.  (Weights fit in int:
+// W <= 4 (N + B) + 2 B.)
+struct SegmentSpan {
+  int nseg;    // segments in use
+  int W;       // total weight
+  int ntiles;  // tiles of this segment
+  int b0, j0;  // request and tile of its first tile
+  int P0;      // weight of the requests before b0
+  __device__ __forceinline__ int segment_of(int x) const { return (int)((int64_t)x * nseg / W); }
+};
+
+// One workgroup's segment, found with two wave-wide scans over the requests
+// (64 per step); every wave computes the same result.  Segment 0 also writes
+// the zero outputs (and piece records) of requests without tokens, for its
+// head group.  Returns false if the segment holds no tile.
+template <int SHIFT, int THREADS>
+__device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int hg, int lane,
+                                             SegmentSpan& sp) {
+  const int N = p.total_tokens;
+  int W = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    const int nt = request_tiles<SHIFT>(p.indptr, c + lane, p.B, N);
+    W += wave_sum_i32(nt > 0 ? TILE_W * nt + START_W : 0);
+    uint64_t empty = seg == 0 ? __ballot(c + lane < p.B && nt == 0) : 0ull;
+    while (empty) {
+      const int b = c + __builtin_ctzll(empty);
+      empty &= empty - 1;
+      if (hg == 0 && threadIdx.x == 0 && p.req_pieces) p.req_pieces[b] = make_int2(0, 0);
+      for (int i = threadIdx.x; i < HEADS * 64; i += THREADS) {
+        const int h = hg * HEADS + (i >> 6);
+        if (h < p.H)
+          *reinterpret_cast<uint4*>(p.out + ((int64_t)b * p.H + h) * V_WIDTH + 8 * (i & 63)) =
+              make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+  const int nseg = min(p.nseg, W / (TILE_W + START_W));
+  if (seg >= nseg) return false;
+  const int x_lo = (int)(((int64_t)seg * W + nseg - 1) / nseg);
+  const int x_hi = (int)(((int64_t)(seg + 1) * W + nseg - 1) / nseg);
+  // global index t0 of the first tile at or after x_lo (its request b0, tile
+  // j0, weight P0 before b0) and t1 of the first at or after x_hi
+  int t0 = -1, t1 = -1, b0 = 0, j0 = 0, P0 = 0;
+  int wcarry = 0, tcarry = 0;
+  for (int c = 0; c < p.B && t1 < 0; c += 64) {
+    const int nt = request_tiles<SHIFT>(p.indptr, c + lane, p.B, N);
+    const int w = nt > 0 ? TILE_W * nt + START_W : 0;
+    const int Pb = wcarry + wave_inclusive_scan(w, lane) - w;
+    const int TB = tcarry + wave_inclusive_scan(nt, lane) - nt;
+    const int last_x = Pb + START_W + TILE_W * (nt - 1);
+    auto first_at = [&](int X, int& t, bool keep) {
+      const uint64_t hit = __ballot(nt > 0 && last_x >= X);
+      if (t >= 0 || !hit) return;
+      const int l = __builtin_ctzll(hit);
+      const int pb = __builtin_amdgcn_readlane(Pb, l);
+      const int rel = X - pb - START_W;
+      const int j = rel <= 0 ? 0 : (rel + TILE_W - 1) / TILE_W;
+      t = __builtin_amdgcn_readlane(TB, l) + j;
+      if (keep) {
+        b0 = c + l;
+        j0 = j;
+        P0 = pb;
+      }
+    };
+    first_at(x_lo, t0, true);
+    first_at(x_hi, t1, false);
+    wcarry += wave_sum_i32(w);
+    tcarry += wave_sum_i32(nt);
+    if (c + 64 >= p.B && t1 < 0) t1 = tcarry;  // past the last tile
+  }
+  sp.nseg = nseg;
+  sp.W = W;
+  sp.ntiles = t0 < 0 ? 0 : t1 - t0;
+  sp.b0 = b0;
+  sp.j0 = j0;
+  sp.P0 = P0;
+  return sp.ntiles > 0;
+}
+
+// Walks the tiles of consecutive requests: request b, tile j of its nt
+// tiles, request range [lo, hi).  Requests without tokens are skipped.  The
+// kv_indptr values come from a 64-entry window held one entry per lane.
+template <int SHIFT>
+struct TileCursor {
+  int b, j, nt, lo, hi;
+  int win, win_val;
+  __device__ __forceinline__ int tile_lo() const { return lo + (j << SHIFT); }
+  __device__ __forceinline__ int tile_hi() const { return min(tile_lo() + (1 << SHIFT), hi); }
+
+  __device__ __forceinline__ void load_window(const SplitParams& p, int first, int lane) {
+    win = first;
+    win_val = clamp_tok(p.indptr[min(first + lane, p.B)], p.total_tokens);
+  }
+  // (every field assigned exactly once on every path, so that the cursor
+  // stays in registers)
+  __device__ __forceinline__ void set_request(const SplitParams& p, int nb, int lane) {
+    const bool valid = nb < p.B;  // past the last request: an empty cursor
+    if (valid && nb + 1 - win > 63) load_window(p, nb, lane);
+    const int l = __builtin_amdgcn_readlane(win_val, valid ? nb - win : 0);
+    const int h = max(l, __builtin_amdgcn_readlane(win_val, valid ? nb + 1 - win : 0));
+    b = nb;
+    lo = valid ? l : 0;
+    hi = valid ? h : 0;
+    nt = valid ? (h - l + (1 << SHIFT) - 1) >> SHIFT : 0;
+  }
+  __device__ __forceinline__ void start(const SplitParams& p, int b0, int j0, int lane) {
+    load_window(p, b0, lane);
+    set_request(p, b0, lane);
+    j = j0;
+  }
+  __device__ __forceinline__ void advance(const SplitParams& p, int lane) {
+    if (++j < nt) return;
+    j = 0;
+    do {
+      set_request(p, b + 1, lane);
+    } while (nt == 0 && b < p.B);
+  }
+};
+
+// ---- explicitly pipelined loads.  Index, query and row copies are issued as
+// inline assembly and waited for with an explicit s_waitcnt vmcnt(N): left to
+// itself the compiler sinks prefetches down to their first use or drains
+// every load at a barrier, which removes the overlap the pipeline exists
+// for.  Loads (register and LDS-destination alike) complete in issue order,
+// so "at most N outstanding" proves every load older than the N youngest
+// done; stores, which the compiler may interleave, only make such a wait
+// stricter.  After a wait, pin() makes the compiler treat the registers as
+// redefined there, so no use of the data can be scheduled above the wait.
+__device__ __forceinline__ int32_t issue_load_i32(const int32_t* p) {
+  int32_t v;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+
+// Global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
+// address lds_base + 16*l (lds_base wave-uniform, passed in M0); lanes
+// outside exec write nothing.  The caller waits with vmcnt.  M0 is not
+// otherwise used by these kernels.
+__device__ __forceinline__ void issue_lds_dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
+}
+
+__device__ __forceinline__ void pin(int32_t& x) { asm volatile("" : "+v"(x)); }
+
+// ---- partial results.  Partial outputs are stored as fp16 (round to
+// nearest even) before the per-tensor scale; the rows this library is fed
+// hold E4M3 values (|v| <= 448), so the partials, convex combinations of
+// them, cannot overflow, and fp16's 11-bit significand is finer than the
+// bf16 the merged output is rounded to.
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w).x; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w).y; }
+
+// Merge of the np partial results (pieces s0 + b .. s0 + np - 1 + b) of
+// request b for one head, by one wave: out = scale * sum_s w_s o_s / sum_s
+// w_s with w_s = 2^(lse_s - max lse).  Pieces are taken eight at a time with
+// all their loads issued together (one memory latency per eight pieces) and
+// folded in with a running maximum.  Lane l produces output columns
+// 8l .. 8l+7.
+__device__ __forceinline__ void merge_pieces(const uint16_t* part_o, const float* part_lse, int Hp,
+                                             int b, int s0, int np, int head, float kv_scale,
+                                             uint16_t* op, int lane) {
+  const float* lse = part_lse + (int64_t)(s0 + b) * Hp + head;  // piece i at lse[i * Hp]
+  const uint16_t* po = part_o + ((int64_t)(s0 + b) * Hp + head) * V_WIDTH + 8 * lane;
+  const int64_t pstride = (int64_t)Hp * V_WIDTH;  // elements between consecutive pieces
+  float M = -INFINITY, den = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < np; base += 8) {
+    const int cnt = min(8, np - base);
+    const float lv = lane < cnt ? lse[(int64_t)(base + lane) * Hp] : -INFINITY;
+    uint4 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)  // u >= cnt re-reads the last piece (in bounds, unused)
+      x[u] = *reinterpret_cast<const uint4*>(po + (int64_t)(base + min(u, cnt - 1)) * pstride);
+    float cm = lv;
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+    const float m_new = fmaxf(M, __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                     __builtin_bit_cast(int, cm))));
+    const float r = __builtin_amdgcn_exp2f(M - m_new);  // 0 on the first chunk
+    den *= r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= r;
+    M = m_new;
+    const float wl = lane < cnt ? __builtin_amdgcn_exp2f(lv - M) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (u < cnt) {
+        const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
+        acc[0] += wgt * f16_lo(x[u].x); acc[1] += wgt * f16_hi(x[u].x);
+        acc[2] += wgt * f16_lo(x[u].y); acc[3] += wgt * f16_hi(x[u].y);
+        acc[4] += wgt * f16_lo(x[u].z); acc[5] += wgt * f16_hi(x[u].z);
+        acc[6] += wgt * f16_lo(x[u].w); acc[7] += wgt * f16_hi(x[u].w);
+        den += wgt;
+      }
+    }
+  }
+  const float inv = kv_scale / den;
+  uint4 v;
+  v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<uint4*>(op + 8 * lane) = v;
+}
+
+}  // namespace decode
+}  // namespace fp8mla

@@ -28,12 +28,23 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 
-DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_tokens, int num_cus);
+// tile_tokens: 128 for the FP8 kernel, 64 for the BF16 one.
+DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_tokens, int num_cus,
+                           int tile_tokens);
 
 hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
                              const int32_t* kv_indptr, const int32_t* kv_indices,
                              int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
                              float sm_scale, uint16_t* out, void* workspace, const DecodePlan& plan,
                              hipStream_t stream);
+
+hipError_t launch_mla_decode_bf16(const uint16_t* q, const uint16_t* kv, int64_t num_rows,
+                                  const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  int64_t total_tokens, int32_t batch, int32_t num_heads,
+                                  float scale, float sm_scale, uint16_t* out, void* workspace,
+                                  const DecodePlan& plan, hipStream_t stream);
+
+constexpr int kFp8TileTokens = 128;
+constexpr int kBf16TileTokens = 64;
 
 }  // namespace fp8mla

@@ -33,19 +33,17 @@
 //    reduction of O.
 // KV bytes move from HBM once per head group; each value byte is converted
 // once per wave that consumes it.
-#include "device_common.h"
-#include "launch.h"
-
-#include <math.h>
+#include "decode_host.h"
 
 namespace fp8mla {
 namespace {
+
+using namespace decode;
 
 constexpr int NWAVES = 8;
 constexpr int THREADS = 64 * NWAVES;              // 512
 constexpr int TILE = 16 * NWAVES;                 // tokens per tile: 16 per wave
 constexpr int TILE_SHIFT = 7;                     // log2(TILE)
-constexpr int HEADS = 16;                         // heads per workgroup
 constexpr int ROW_SLOTS = KV_CHUNKS + 1;          // 16-byte LDS slots per row: 36 + 1 pad (odd)
 constexpr int ROWB = 16 * ROW_SLOTS;              // 592 LDS bytes per row
 constexpr int TILE_BYTES = TILE * ROWB;           // 75776
@@ -53,167 +51,7 @@ constexpr int KSTEPS = KV_WIDTH / 64;             // 16-byte K reads per lane pe
 constexpr int QSTEPS = 2 * KSTEPS;                // 18 MFMA steps of 32 dims over 576
 constexpr int DMA_OPS = (16 * ROW_SLOTS + 63) / 64;  // LDS-copy ops per wave per tile: 10
 static_assert(TILE == 1 << TILE_SHIFT, "tile size");
-constexpr int TILE_W = 4;   // segment balancing: weight of a tile
-constexpr int START_W = 2;  // extra weight of a request's first tile
 
-struct SplitParams {
-  const uint16_t* q;
-  const uint8_t* pool;
-  const int32_t* indptr;
-  const int32_t* indices;
-  uint16_t* out;
-  uint16_t* part_o;  // fp16 bits
-  float* part_lse;
-  int2* req_pieces;  // per request: (segment of its first piece, number of pieces)
-  uint32_t max_slot;
-  int32_t total_tokens;
-  int32_t B;
-  int32_t H;
-  int32_t HG;
-  int32_t Hp;
-  int32_t nseg;     // segments the tile list is cut into
-  int32_t items;    // nseg * HG
-  int32_t xcd_per;
-  float score_scale;  // sm_scale * scale * log2(e): scores in the base-2 domain
-  float kv_scale;
-};
-
-__device__ __forceinline__ float wave_max_over_groups(float x) {
-  // lanes h, h+16, h+32, h+48 hold the same head
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum_over_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
-}
-
-__device__ __forceinline__ int clamp_tok(int v, int n) { return v < 0 ? 0 : (v > n ? n : v); }
-
-// ---- request tiles.  Request b covers tokens [lo_b, hi_b) with
-// lo_b = clamp(kv_indptr[b], 0, N) and hi_b = max(lo_b, clamp(kv_indptr[b+1],
-// 0, N)), and has ceil((hi_b - lo_b) / 128) tiles.
-__device__ __forceinline__ int request_tiles(const int32_t* indptr, int b, int B, int N) {
-  if (b >= B) return 0;
-  const int lo = clamp_tok(indptr[b], N);
-  const int hi = max(lo, clamp_tok(indptr[b + 1], N));
-  return (hi - lo + TILE - 1) >> TILE_SHIFT;
-}
-
-__device__ __forceinline__ int wave_sum_i32(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
-// Merge of the np partial results (pieces s0 + b .. s0 + np - 1 + b) of
-// request b for one head, by one wave: out = scale * sum_s w_s o_s / sum_s
-// w_s with w_s = 2^(lse_s - max lse).  Pieces are taken eight at a time with
-// all their loads issued together (one memory latency per eight pieces) and
-// folded in with a running maximum.  Lane l produces output columns
-// 8l .. 8l+7.
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
-
-// Partial outputs are stored as fp16 (round to nearest even), in E4M3 units
-// (before the per-tensor scale): every partial is a convex combination of
-// E4M3 values, |o| <= 448, so fp16 cannot overflow, and its 11-bit
-// significand is finer than the bf16 the merged output is rounded to.
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w).x; }
-__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w).y; }
-
-__device__ __forceinline__ void merge_pieces(const uint16_t* part_o, const float* part_lse, int Hp,
-                                             int b, int s0, int np, int head, float kv_scale,
-                                             uint16_t* op, int lane) {
-  const float* lse = part_lse + (int64_t)(s0 + b) * Hp + head;  // piece i at lse[i * Hp]
-  const uint16_t* po = part_o + ((int64_t)(s0 + b) * Hp + head) * V_WIDTH + 8 * lane;
-  const int64_t pstride = (int64_t)Hp * V_WIDTH;  // elements between consecutive pieces
-  float M = -INFINITY, den = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int base = 0; base < np; base += 8) {
-    const int cnt = min(8, np - base);
-    const float lv = lane < cnt ? lse[(int64_t)(base + lane) * Hp] : -INFINITY;
-    uint4 x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)  // u >= cnt re-reads the last piece (in bounds, unused)
-      x[u] = *reinterpret_cast<const uint4*>(po + (int64_t)(base + min(u, cnt - 1)) * pstride);
-    float cm = lv;
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
-    const float m_new = fmaxf(M, __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-                                     __builtin_bit_cast(int, cm))));
-    const float r = __builtin_amdgcn_exp2f(M - m_new);  // 0 on the first chunk
-    den *= r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= r;
-    M = m_new;
-    const float wl = lane < cnt ? __builtin_amdgcn_exp2f(lv - M) : 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (u < cnt) {
-        const float wgt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), u));
-        acc[0] += wgt * f16_lo(x[u].x); acc[1] += wgt * f16_hi(x[u].x);
-        acc[2] += wgt * f16_lo(x[u].y); acc[3] += wgt * f16_hi(x[u].y);
-        acc[4] += wgt * f16_lo(x[u].z); acc[5] += wgt * f16_hi(x[u].z);
-        acc[6] += wgt * f16_lo(x[u].w); acc[7] += wgt * f16_hi(x[u].w);
-        den += wgt;
-      }
-    }
-  }
-  const float inv = kv_scale / den;
-  uint4 v;
-  v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-  v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-  *reinterpret_cast<uint4*>(op + 8 * lane) = v;
-}
-
-// ---- explicitly pipelined loads.  Index, query and row copies are issued as
-// inline assembly and waited for with an explicit s_waitcnt vmcnt(N): left to
-// itself the compiler sinks prefetches down to their first use or drains
-// every load at a barrier, which removes the overlap the pipeline exists
-// for.  Loads (register and LDS-destination alike) complete in issue order,
-// so "at most N outstanding" proves every load older than the N youngest
-// done; stores, which the compiler may interleave, only make such a wait
-// stricter.  After a wait, pin() makes the compiler treat the registers as
-// redefined there, so no use of the data can be scheduled above the wait.
-__device__ __forceinline__ int32_t issue_load_i32(const int32_t* p) {
-  int32_t v;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(v) : "v"(p));
-  return v;
-}
-
-// Global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
-// address lds_base + 16*l (lds_base wave-uniform, passed in M0); lanes
-// outside exec write nothing.  The caller waits with vmcnt.  M0 is not
-// otherwise used by these kernels.
-__device__ __forceinline__ void issue_lds_dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(g), "s"(lds_base)
-               : "memory", "m0");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));
-}
 
 // Wait until at most n vector-memory operations are outstanding (n is
 // wave-uniform and one of the counts the pipeline produces; any other value
@@ -227,22 +65,10 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
   }
 }
 
-__device__ __forceinline__ void pin(int32_t& x) { asm volatile("" : "+v"(x)); }
-
 // Token row (tile-relative) held by MFMA row m of wave w.  Odd waves use
 // row m ^ 12 so that the transposed LDS reads of two consecutive waves'
 // rows fall in distinct banks.
 __device__ __forceinline__ int tile_row(int w, int m) { return 16 * w + ((w & 1) ? (m ^ 12) : m); }
-
-// Walks the tiles of consecutive requests: request b, tile j of its nt
-// tiles, request range [lo, hi).  Requests without tokens are skipped.  The
-// kv_indptr values come from a 64-entry window held one entry per lane.
-struct TileCursor {
-  int b, j, nt, lo, hi;
-  int win, win_val;
-  __device__ __forceinline__ int tile_lo() const { return lo + (j << TILE_SHIFT); }
-  __device__ __forceinline__ int tile_hi() const { return min(tile_lo() + TILE, hi); }
-};
 
 __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p) {
   // Two row tiles (the one being computed and the next one landing) and the
@@ -262,108 +88,16 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   if (item >= p.items) return;
   const int seg = item / p.HG;
   const int hg = item - seg * p.HG;
-  const int N = p.total_tokens;
   const int head = hg * HEADS + t;  // head whose scores / outputs this lane carries
 
-  // ---- this segment's tiles.  Tiles are weighted by their cost: TILE_W per
-  // tile and START_W more for the first tile of a request (the query switch
-  // and the extra output).  Request b's tile j sits at weighted position
-  // x = P_b + START_W + TILE_W * j, P_b being the total weight of the
-  // requests before b; segment s takes the tiles with x in
-  // [ceil(s W / nseg), ceil((s+1) W / nseg)), W the total weight, so tile x
-  // belongs to segment floor(x nseg / W).  Found with two wave-wide scans
-  // over the requests, 64 per step: the global index t0 of the first tile,
-  // its request b0 and tile j0, and the number of tiles.
-  // (Weights fit in int: W <= 4 * (N / 128 + B) + 2 * B.)
-  int W = 0;
-  for (int c = 0; c < p.B; c += 64) {
-    const int nt = request_tiles(p.indptr, c + lane, p.B, N);
-    W += wave_sum_i32(nt > 0 ? TILE_W * nt + START_W : 0);
-    // requests without tokens: zero outputs, written by the first segment
-    uint64_t empty = seg == 0 ? __ballot(c + lane < p.B && nt == 0) : 0ull;
-    while (empty) {
-      const int b = c + __builtin_ctzll(empty);
-      empty &= empty - 1;
-      if (hg == 0 && threadIdx.x == 0 && p.req_pieces) p.req_pieces[b] = make_int2(0, 0);
-      for (int i = threadIdx.x; i < HEADS * 64; i += THREADS) {
-        const int h = hg * HEADS + (i >> 6);
-        if (h < p.H)
-          *reinterpret_cast<uint4*>(p.out + ((int64_t)b * p.H + h) * V_WIDTH + 8 * (i & 63)) =
-              make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  }
-  // Consecutive tile positions are at most TILE_W + START_W apart, so with
-  // segments at least that wide every segment holds a tile and the pieces of
-  // a request are consecutive segments; later workgroups stay idle.
-  const int nseg = min(p.nseg, W / (TILE_W + START_W));
-  if (seg >= nseg) return;
-  const int x_lo = (int)(((int64_t)seg * W + nseg - 1) / nseg);
-  const int x_hi = (int)(((int64_t)(seg + 1) * W + nseg - 1) / nseg);
-  auto segment_of = [&](int x) -> int { return (int)((int64_t)x * nseg / W); };
-  // global index t0 of the first tile at or after x_lo (its request b0, tile
-  // j0, weight P0 before b0) and t1 of the first at or after x_hi
-  int t0 = -1, t1 = -1, b0 = 0, j0 = 0, P0 = 0;
-  {
-    int wcarry = 0, tcarry = 0;
-    for (int c = 0; c < p.B && t1 < 0; c += 64) {
-      const int nt = request_tiles(p.indptr, c + lane, p.B, N);
-      const int w = nt > 0 ? TILE_W * nt + START_W : 0;
-      const int Pb = wcarry + wave_inclusive_scan(w, lane) - w;
-      const int TB = tcarry + wave_inclusive_scan(nt, lane) - nt;
-      const int last_x = Pb + START_W + TILE_W * (nt - 1);
-      auto first_at = [&](int X, int& t, bool keep) {
-        const uint64_t hit = __ballot(nt > 0 && last_x >= X);
-        if (t >= 0 || !hit) return;
-        const int l = __builtin_ctzll(hit);
-        const int pb = __builtin_amdgcn_readlane(Pb, l);
-        const int rel = X - pb - START_W;
-        const int j = rel <= 0 ? 0 : (rel + TILE_W - 1) / TILE_W;
-        t = __builtin_amdgcn_readlane(TB, l) + j;
-        if (keep) {
-          b0 = c + l;
-          j0 = j;
-          P0 = pb;
-        }
-      };
-      first_at(x_lo, t0, true);
-      first_at(x_hi, t1, false);
-      wcarry += wave_sum_i32(w);
-      tcarry += wave_sum_i32(nt);
-      if (c + 64 >= p.B && t1 < 0) t1 = tcarry;  // past the last tile
-    }
-  }
-  if (t0 < 0) return;
-  const int ntiles = t1 - t0;
-  if (ntiles <= 0) return;
-  auto load_window = [&](TileCursor& c, int b) {
-    c.win = b;
-    c.win_val = clamp_tok(p.indptr[min(b + lane, p.B)], N);
-  };
-  // (every field assigned exactly once on every path, so that the cursors
-  // stay in registers)
-  auto set_request = [&](TileCursor& c, int b) {
-    const bool valid = b < p.B;  // past the last request: an empty cursor
-    if (valid && b + 1 - c.win > 63) load_window(c, b);
-    const int lo = __builtin_amdgcn_readlane(c.win_val, valid ? b - c.win : 0);
-    const int hi = max(lo, __builtin_amdgcn_readlane(c.win_val, valid ? b + 1 - c.win : 0));
-    c.b = b;
-    c.lo = valid ? lo : 0;
-    c.hi = valid ? hi : 0;
-    c.nt = valid ? (hi - lo + TILE - 1) >> TILE_SHIFT : 0;
-  };
-  auto advance = [&](TileCursor& c) {
-    if (++c.j < c.nt) return;
-    c.j = 0;
-    do {
-      set_request(c, c.b + 1);
-    } while (c.nt == 0 && c.b < p.B);
-  };
-  TileCursor cc;  // tile being computed
-  load_window(cc, b0);
-  set_request(cc, b0);
-  cc.j = j0;
-  TileCursor lc = cc;  // next tile whose index is loaded
+  // ---- this segment's tiles (cost-weighted split of the list of all
+  // requests' tiles), and a cursor over them
+  SegmentSpan span;
+  if (!find_segment<TILE_SHIFT, THREADS>(p, seg, hg, lane, span)) return;
+  const int ntiles = span.ntiles;
+  TileCursor<TILE_SHIFT> cc;  // tile being computed
+  cc.start(p, span.b0, span.j0, lane);
+  TileCursor<TILE_SHIFT> lc = cc;  // next tile whose index is loaded
 
   // ---- row tiles.  Tile k of the segment goes to LDS slot k & 1 by
   // global->LDS copies, two tiles ahead of use.  Token r of the tile is LDS
@@ -389,7 +123,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     const int tok = tlo + 16 * w + t;
     const int32_t* a = lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) : p.indices;
     const int32_t v = issue_load_i32(a);
-    advance(lc);
+    lc.advance(p, lane);
     return v;
   };
   const uint32_t lds_tiles = (uint32_t)(uintptr_t)(
@@ -483,15 +217,15 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   for (int c = 0; c < 4; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   float l_w = 0.f;
-  bool whole_request = j0 == 0;  // the current request's first tile is in this segment
-  int P_cur = P0;                 // weight of the requests before the current one
+  bool whole_request = span.j0 == 0;  // the current request's first tile is in this segment
+  int P_cur = span.P0;                 // weight of the requests before the current one
   // Pieces of a request: the segments its tiles [first, first + nt) fall in.
   // Recorded for the combine by the workgroup holding the request's first
   // tile (head group 0).
   auto record_pieces = [&]() {
     if (hg == 0 && threadIdx.x == 0) {
-      const int s0 = segment_of(P_cur + START_W);
-      const int s1 = segment_of(P_cur + START_W + TILE_W * (cc.nt - 1));
+      const int s0 = span.segment_of(P_cur + START_W);
+      const int s1 = span.segment_of(P_cur + START_W + TILE_W * (cc.nt - 1));
       p.req_pieces[cc.b] = make_int2(s0, s1 - s0 + 1);
     }
   };
@@ -588,9 +322,9 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     ix_next = load_next_index();
     const bool new_q = last_of_request && k + 1 < ntiles;
     const bool rows_now = k + 2 < ntiles && (!new_q || w >= 2);
-    TileCursor nc = cc;
+    TileCursor<TILE_SHIFT> nc = cc;
     if (new_q) {
-      advance(nc);
+      nc.advance(p, lane);
       issue_query_copy(nc.b, lds_tiles + (uint32_t)((k & 1) * TILE_BYTES));
     }
     if (rows_now) issue_tile(k + 2, ix_cur);
@@ -648,7 +382,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       whole_request = true;
       record_pieces();
     } else {
-      advance(cc);
+      cc.advance(p, lane);
     }
   };
 
@@ -688,17 +422,19 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const CombineParams p)
 
 }  // namespace
 
-DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_tokens, int num_cus) {
+DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_tokens, int num_cus,
+                           int tile_tokens) {
   DecodePlan pl{};
   pl.HG = (num_heads + HEADS - 1) / HEADS;
   pl.Hp = pl.HG * HEADS;
-  // One 8-wave workgroup per compute unit in flight; head groups of a
-  // segment are separate workgroups that share the segment's rows through
-  // L2.  The tile list has at most ceil(N / 128) + batch tiles, so more
-  // segments than that would stay empty.
+  // One workgroup per compute unit in flight; head groups of a segment are
+  // separate workgroups that share the segment's rows through L2.  The tile
+  // list has at most ceil(N / tile) + batch tiles, so more segments than
+  // that would stay empty.
   int64_t nseg = num_cus / pl.HG;
   if (nseg < 1) nseg = 1;
-  const int64_t max_tiles = (total_tokens > 0 ? (total_tokens + TILE - 1) / TILE : 0) + batch;
+  const int64_t max_tiles =
+      (total_tokens > 0 ? (total_tokens + tile_tokens - 1) / tile_tokens : 0) + batch;
   if (nseg > max_tiles) nseg = max_tiles;
   if (nseg < 1) nseg = 1;
   pl.nseg = (int32_t)nseg;
@@ -723,15 +459,15 @@ DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_token
   return pl;
 }
 
-hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
-                             const int32_t* kv_indptr, const int32_t* kv_indices,
-                             int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
-                             float sm_scale, uint16_t* out, void* workspace, const DecodePlan& pl,
-                             hipStream_t stream) {
+decode::SplitParams make_split_params(const uint16_t* q, const void* kv_rows, int64_t num_slots,
+                                      const int32_t* kv_indptr, const int32_t* kv_indices,
+                                      int64_t total_tokens, int32_t batch, int32_t num_heads,
+                                      float scale, float sm_scale, uint16_t* out,
+                                      void* workspace, const DecodePlan& pl) {
   char* ws = reinterpret_cast<char*>(workspace);
-  SplitParams sp;
+  decode::SplitParams sp;
   sp.q = q;
-  sp.pool = kv_pool;
+  sp.pool = reinterpret_cast<const uint8_t*>(kv_rows);
   sp.indptr = kv_indptr;
   sp.indices = kv_indices;
   sp.out = out;
@@ -749,19 +485,34 @@ hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t 
   sp.xcd_per = pl.xcd_per;
   sp.score_scale = (float)((double)sm_scale * (double)scale * 1.4426950408889634);
   sp.kv_scale = scale;
+  return sp;
+}
+
+hipError_t launch_mla_combine(const decode::SplitParams& sp, hipStream_t stream) {
+  CombineParams cp;
+  cp.req_pieces = sp.req_pieces;
+  cp.part_o = sp.part_o;
+  cp.part_lse = sp.part_lse;
+  cp.out = sp.out;
+  cp.H = sp.H;
+  cp.Hp = sp.Hp;
+  cp.kv_scale = sp.kv_scale;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(sp.B, (sp.H + 3) / 4), dim3(256), 0, stream, cp);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                             const int32_t* kv_indptr, const int32_t* kv_indices,
+                             int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
+                             float sm_scale, uint16_t* out, void* workspace, const DecodePlan& pl,
+                             hipStream_t stream) {
+  const decode::SplitParams sp = make_split_params(q, kv_pool, num_slots, kv_indptr, kv_indices,
+                                                   total_tokens, batch, num_heads, scale,
+                                                   sm_scale, out, workspace, pl);
   hipLaunchKernelGGL(mla_split_kernel, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || total_tokens == 0) return e;  // no tokens: nothing to merge
-  CombineParams cp;
-  cp.req_pieces = reinterpret_cast<const int2*>(ws);
-  cp.part_o = sp.part_o;
-  cp.part_lse = sp.part_lse;
-  cp.out = out;
-  cp.H = num_heads;
-  cp.Hp = pl.Hp;
-  cp.kv_scale = scale;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(batch, (num_heads + 3) / 4), dim3(256), 0, stream, cp);
-  return hipGetLastError();
+  return launch_mla_combine(sp, stream);
 }
 
 }  // namespace fp8mla

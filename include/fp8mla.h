@@ -134,6 +134,32 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
  */
 size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens);
 
+/*
+ * mla_decode_bf16 -- the same decode over BF16 latent rows: the attention
+ * that follows a cast on the pages' fallback paths ("The Gather-Then-Cast
+ * Pivot", Reasoning Process: gather, cast, attend over indices 0..n-1; "The
+ * KV Cache Cast Bottleneck", The Context: cast the whole pool, attend with
+ * the original indices).  Benchmark-only: it lets those paths be timed end to
+ * end against mla_decode_fp8.
+ *
+ * Computes exactly what mla_decode_fp8 computes with K[t,:] = scale *
+ * kv[kv_indices[t], :] read as BF16 instead of E4M3FN.
+ *   kv          uint16 [num_rows, 576]  BF16 latent rows (e.g. the output of
+ *                                       cast_pool_fp8_bf16 or gather_cast_fp8_bf16);
+ *                                       values must lie within the fp16 range
+ *                                       (|v| <= 65504), which cast E4M3 rows do
+ *   num_rows    rows of kv (>= 1 unless total_tokens == 0)
+ *   workspace   at least mla_decode_bf16_workspace_bytes(...) bytes of scratch
+ * All other arguments, layouts, ownership and status codes as mla_decode_fp8.
+ */
+int mla_decode_bf16(const uint16_t* q, const uint16_t* kv, int64_t num_rows,
+                    const int32_t* kv_indptr, const int32_t* kv_indices, int64_t total_tokens,
+                    int32_t batch, int32_t num_heads, float scale, float sm_scale,
+                    uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace size in bytes for mla_decode_bf16 (as mla_decode_fp8_workspace_bytes). */
+size_t mla_decode_bf16_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens);
+
 /* Static description of a status code; never NULL. */
 const char* fp8mla_status_string(int status);
 

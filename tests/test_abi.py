@@ -127,6 +127,31 @@ def test_mla_decode_validation():
     assert _decode(lib, indptr=P16 + 2) == ERR_ALIGN
 
 
+def test_mla_decode_bf16_validation():
+    lib = _lib()
+    lib.mla_decode_bf16.argtypes = lib.mla_decode_fp8.argtypes
+    lib.mla_decode_bf16.restype = ctypes.c_int
+
+    def dec(**kw):
+        a = dict(q=P16, kv=P16, rows=100, indptr=P16, indices=P16, total=10, B=2, H=16,
+                 scale=1.0, sm=0.07, out=P16, ws=P16, ws_bytes=1 << 20, stream=NULL)
+        a.update(kw)
+        return lib.mla_decode_bf16(a["q"], a["kv"], a["rows"], a["indptr"], a["indices"],
+                                   a["total"], a["B"], a["H"], a["scale"], a["sm"], a["out"],
+                                   a["ws"], a["ws_bytes"], a["stream"])
+
+    assert dec(B=0) == ERR_SHAPE
+    assert dec(H=257) == ERR_SHAPE
+    assert dec(rows=0) == ERR_SHAPE
+    assert dec(total=-1) == ERR_SHAPE
+    assert dec(scale=0.0) == ERR_SCALAR
+    assert dec(sm=math.nan) == ERR_SCALAR
+    assert dec(kv=NULL) == ERR_NULL
+    assert dec(ws=NULL) == ERR_NULL
+    assert dec(kv=P8) == ERR_ALIGN
+    assert dec(out=P8) == ERR_ALIGN
+
+
 def test_workspace_query_rejects_bad_sizes():
     lib = _lib()
     assert lib.mla_decode_fp8_workspace_bytes(0, 16, 10) == 0
