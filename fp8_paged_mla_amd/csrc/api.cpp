@@ -88,7 +88,8 @@ size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t 
   if (total_tokens == 0) return 0;
   const int cus = current_device_cus();
   if (cus <= 0) return 0;
-  return fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::kFp8TileTokens)
+  return fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus,
+                                 fp8mla::fp8_decode_kernel(num_heads, total_tokens, cus))
       .workspace_bytes;
 }
 
@@ -108,8 +109,8 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
     return FP8MLA_ERR_MISALIGNED;
   const int cus = current_device_cus();
   if (cus <= 0) return FP8MLA_ERR_HIP;
-  const fp8mla::DecodePlan plan =
-      fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::kFp8TileTokens);
+  const fp8mla::DecodePlan plan = fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus,
+                                                          fp8mla::fp8_decode_kernel(num_heads, total_tokens, cus));
   if (total_tokens > 0 && workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
   const hipError_t e = fp8mla::launch_mla_decode(q, kv_pool, num_slots, kv_indptr, kv_indices,
                                                  total_tokens, batch, num_heads, scale, sm_scale,
@@ -125,7 +126,7 @@ size_t mla_decode_bf16_workspace_bytes(int32_t batch, int32_t num_heads, int64_t
   if (total_tokens == 0) return 0;
   const int cus = current_device_cus();
   if (cus <= 0) return 0;
-  return fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::kBf16TileTokens)
+  return fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::DecodeKernel::kBf16)
       .workspace_bytes;
 }
 
@@ -146,7 +147,7 @@ int mla_decode_bf16(const uint16_t* q, const uint16_t* kv, int64_t num_rows,
   const int cus = current_device_cus();
   if (cus <= 0) return FP8MLA_ERR_HIP;
   const fp8mla::DecodePlan plan =
-      fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::kBf16TileTokens);
+      fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::DecodeKernel::kBf16);
   if (total_tokens > 0 && workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
   const hipError_t e = fp8mla::launch_mla_decode_bf16(q, kv, num_rows, kv_indptr, kv_indices,
                                                       total_tokens, batch, num_heads, scale,

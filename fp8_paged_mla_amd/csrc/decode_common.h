@@ -99,8 +99,8 @@ struct SegmentSpan {
 // One workgroup's segment, found with two wave-wide scans over the requests
 // (64 per step); every wave computes the same result.  Segment 0 also writes
 // the zero outputs (and piece records) of requests without tokens, for its
-// head group.  Returns false if the segment holds no tile.
-template <int SHIFT, int THREADS>
+// WG_HEADS heads (head set hg).  Returns false if the segment holds no tile.
+template <int SHIFT, int THREADS, int WG_HEADS = HEADS>
 __device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int hg, int lane,
                                              SegmentSpan& sp) {
   const int N = p.total_tokens;
@@ -113,8 +113,8 @@ __device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int 
       const int b = c + __builtin_ctzll(empty);
       empty &= empty - 1;
       if (hg == 0 && threadIdx.x == 0 && p.req_pieces) p.req_pieces[b] = make_int2(0, 0);
-      for (int i = threadIdx.x; i < HEADS * 64; i += THREADS) {
-        const int h = hg * HEADS + (i >> 6);
+      for (int i = threadIdx.x; i < WG_HEADS * 64; i += THREADS) {
+        const int h = hg * WG_HEADS + (i >> 6);
         if (h < p.H)
           *reinterpret_cast<uint4*>(p.out + ((int64_t)b * p.H + h) * V_WIDTH + 8 * (i & 63)) =
               make_uint4(0u, 0u, 0u, 0u);

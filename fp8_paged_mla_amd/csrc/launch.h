@@ -16,9 +16,23 @@ hipError_t launch_gather_cast(const uint8_t* pool, int64_t num_slots, const int3
 
 // Decode schedule: equal segments of the request-tile list x head groups, and the split-K
 // workspace layout (per-request piece ranges, partial outputs, log2-sum-exp values).
+// Which split kernel a decode call runs: FP8 rows with 16 heads per
+// workgroup, FP8 rows with 64 heads per workgroup (64 or more heads), or
+// BF16 rows.
+enum class DecodeKernel { kFp8, kFp8H64, kBf16 };
+
+// FP8 calls with at least this many heads use the 64-head workgroups, when
+// there is enough work for them: at least kH64MinTilesPerCu 64-token tiles
+// per workgroup slot (CUs / head sets).  With fewer tokens the 16-head
+// kernel, which has four times as many workgroups per segment, exposes more
+// parallelism.
+constexpr int kH64MinHeads = 64;
+constexpr int kH64MinTilesPerCu = 4;
+
 struct DecodePlan {
-  int32_t HG;          // head groups of 16
-  int32_t Hp;          // padded head count = 16 * HG
+  DecodeKernel kernel;
+  int32_t HG;          // head groups (of 16, or of 64 for kFp8H64)
+  int32_t Hp;          // padded head count = HG * heads per workgroup
   int32_t nseg;        // segments the list of request tiles is cut into
   int32_t items;       // nseg * HG workgroups doing work
   int32_t xcd_per;     // work items per XCD slot of the launch grid
@@ -28,9 +42,16 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 
-// tile_tokens: 128 for the FP8 kernel, 64 for the BF16 one.
 DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_tokens, int num_cus,
-                           int tile_tokens);
+                           DecodeKernel kernel);
+
+inline DecodeKernel fp8_decode_kernel(int32_t num_heads, int64_t total_tokens, int num_cus) {
+  if (num_heads < kH64MinHeads) return DecodeKernel::kFp8;
+  const int64_t head_sets = (num_heads + 63) / 64;
+  const int64_t tiles = (total_tokens + 63) / 64;
+  return tiles >= (int64_t)kH64MinTilesPerCu * num_cus / head_sets ? DecodeKernel::kFp8H64
+                                                                  : DecodeKernel::kFp8;
+}
 
 hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
                              const int32_t* kv_indptr, const int32_t* kv_indices,
@@ -44,7 +65,14 @@ hipError_t launch_mla_decode_bf16(const uint16_t* q, const uint16_t* kv, int64_t
                                   float scale, float sm_scale, uint16_t* out, void* workspace,
                                   const DecodePlan& plan, hipStream_t stream);
 
+hipError_t launch_mla_decode_h64(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                                 const int32_t* kv_indptr, const int32_t* kv_indices,
+                                 int64_t total_tokens, int32_t batch, int32_t num_heads,
+                                 float scale, float sm_scale, uint16_t* out, void* workspace,
+                                 const DecodePlan& plan, hipStream_t stream);
+
 constexpr int kFp8TileTokens = 128;
+constexpr int kH64TileTokens = 64;
 constexpr int kBf16TileTokens = 64;
 
 }  // namespace fp8mla

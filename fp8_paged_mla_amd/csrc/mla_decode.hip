@@ -423,10 +423,15 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const CombineParams p)
 }  // namespace
 
 DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_tokens, int num_cus,
-                           int tile_tokens) {
+                           DecodeKernel kernel) {
+  const int tile_tokens = kernel == DecodeKernel::kBf16 ? kBf16TileTokens
+                          : kernel == DecodeKernel::kFp8H64 ? kH64TileTokens
+                                                            : kFp8TileTokens;
+  const int wg_heads = kernel == DecodeKernel::kFp8H64 ? 64 : HEADS;
   DecodePlan pl{};
-  pl.HG = (num_heads + HEADS - 1) / HEADS;
-  pl.Hp = pl.HG * HEADS;
+  pl.kernel = kernel;
+  pl.HG = (num_heads + wg_heads - 1) / wg_heads;
+  pl.Hp = pl.HG * wg_heads;
   // One workgroup per compute unit in flight; head groups of a segment are
   // separate workgroups that share the segment's rows through L2.  The tile
   // list has at most ceil(N / tile) + batch tiles, so more segments than
@@ -506,6 +511,9 @@ hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t 
                              int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
                              float sm_scale, uint16_t* out, void* workspace, const DecodePlan& pl,
                              hipStream_t stream) {
+  if (pl.kernel == DecodeKernel::kFp8H64)
+    return launch_mla_decode_h64(q, kv_pool, num_slots, kv_indptr, kv_indices, total_tokens, batch,
+                                 num_heads, scale, sm_scale, out, workspace, pl, stream);
   const decode::SplitParams sp = make_split_params(q, kv_pool, num_slots, kv_indptr, kv_indices,
                                                    total_tokens, batch, num_heads, scale,
                                                    sm_scale, out, workspace, pl);

@@ -52,6 +52,37 @@ def test_ragged_lengths(dev, lengths):
     _check_full(w, str(lengths))
 
 
+# 64 or more heads with enough tokens (at least 4 64-token tiles per
+# workgroup slot: 4 * CUs / ceil(H / 64) tiles) run the 64-heads-per-workgroup
+# kernel.  Sizes just above that threshold cover padding (80 = 64 + 16),
+# several head sets, ragged and empty requests, many short requests (many
+# query switches) and requests spanning many segments.
+def _h64_tokens(H):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return 64 * (4 * cus // ((H + 63) // 64)) + 64
+
+
+@pytest.mark.parametrize("H,shape", [
+    (64, "two_long"),
+    (80, "ragged"),
+    (128, "ragged"),
+    (128, "many_short"),
+    (256, "two_long"),
+])
+def test_high_head_counts(dev, H, shape):
+    need = _h64_tokens(H)
+    if shape == "two_long":
+        lengths = [need // 2 + 37, 1, 0, need // 2 + 5]
+    elif shape == "ragged":
+        lengths = [need // 3, 63, 0, 65, need // 3 + 1, need // 3 + 200]
+    else:
+        lengths = [300 + (7 * i) % 64 for i in range(need // 300 + 2)]
+    assert sum(lengths) >= need
+    w = workloads.small(len(lengths), H, lengths, seed=H + len(lengths), device=dev)
+    e = _check_full(w, "H=%d %s" % (H, shape))
+    print("H=%d %s tokens=%d" % (H, shape, sum(lengths)), e)
+
+
 def test_all_requests_empty(dev):
     w = workloads.small(4, 16, [0, 0, 0, 0], num_slots=64, device=dev)
     out = _run(w)
