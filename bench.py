@@ -72,7 +72,7 @@ def read_traffic(launch_units):
         return None
 
 
-def cpu_baseline(w, budget_s=15.0):
+def cpu_baseline(w, label, budget_s=15.0):
     """The float64 oracle on the host over the same workload: its requests one
     by one, in repeated passes over the batch, until about budget_s seconds
     have run (at least one full pass)."""
@@ -108,8 +108,8 @@ def cpu_baseline(w, budget_s=15.0):
         "cores": cores,
         "kind": "oracle",
         "sample": "float64 numpy oracle (BLAS on up to %d threads), %d passes over the %d "
-                  "requests (%d tokens each pass) of the batch-40 workload's replica 0: %d "
-                  "tokens in %.1f s" % (cores, passes, w.B, tokens // max(passes, 1), tokens, dt),
+                  "requests (%d tokens each pass) of replica 0 of the %s workload: %d tokens "
+                  "in %.1f s" % (cores, passes, w.B, tokens // max(passes, 1), label, tokens, dt),
     }
 
 
@@ -226,7 +226,7 @@ def main():
     if not args.no_secondary:
         result["secondary"] = secondary(fm, reps, outs, wss, stream, dev, args)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(base)
+        result["cpu_baseline"] = cpu_baseline(base, workloads.CONFIG_NAMES[args.config].split(":")[0])
     print(json.dumps(result), flush=True)
 
 
