@@ -16,6 +16,9 @@ What it computes, and where the pages define it:
   ("The KV Cache Cast Bottleneck", *The Context* and *The Message*) and the
   gather-then-cast of only the slots named by ``kv_indices``
   ("The Gather-Then-Cast Pivot", *Reasoning Process*).
+* ``encode``: the write path, BF16 rows into the FP8 cache by a dtype copy
+  ("When a Faster Kernel Doesn't Speed Up Serving", *Step 3*, CastToFP8),
+  with torch's float -> ``Float8_e4m3fn`` rounding rule.
 * ``attention``: MLA decode over the absorbed latent cache -- one KV head of
   width 576 = 512 latent + 64 rope shared by all query heads, scores over all
   576 dims, values from the first 512 ("The KV Cache Cast Bottleneck",
@@ -28,6 +31,7 @@ the full serving shapes have no printed values on the pages; they rest on
 those pins.
 """
 from .e4m3 import decode_table, e4m3fn_value, bf16_bits_of, cast_table_bf16
+from .encode import encode_e4m3fn, scatter_ref
 from .cast import cast_ref, gather_ref
 from .attention import (
     bf16_bits_to_f64,
@@ -45,6 +49,8 @@ __all__ = [
     "cast_table_bf16",
     "cast_ref",
     "gather_ref",
+    "encode_e4m3fn",
+    "scatter_ref",
     "bf16_bits_to_f64",
     "mla_decode_ref",
     "mla_decode_partial_ref",
