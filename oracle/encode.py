@@ -16,6 +16,11 @@ torch's own conversion in the tests, is:
 * NaN and infinities give NaN; the sign bit is kept in every case (so
   -0 -> 0x80 and negative overflow -> 0xFF).
 
+``saturate=True`` is the other common writer convention for an FP8 KV cache:
+magnitudes are first clamped to 448, so overflow and infinities give +-448
+(0x7E / 0xFE) instead of NaN, while NaN stays NaN; below 448 the two modes
+agree.  The pages' ``copy_`` is the default, ``saturate=False``.
+
 ``scatter_ref`` applies it row by row: pool row ``slots[r]`` receives the
 encoded BF16 row ``r`` times ``inv_scale``; the product is taken in float32
 (round to nearest even), as the kernel does, so that both sides decide each
@@ -42,24 +47,26 @@ def _positive_values() -> np.ndarray:
     return _POS
 
 
-def encode_e4m3fn(y) -> np.ndarray:
+def encode_e4m3fn(y, saturate: bool = False) -> np.ndarray:
     """uint8 E4M3FN codes of float values (any shape), by the rule above."""
     with np.errstate(invalid="ignore"):    # signalling NaN inputs are expected
         y = np.asarray(y, dtype=np.float64)
     table = _positive_values()
-    mag = np.abs(y)
     sign = np.signbit(y).astype(np.uint8) << 7
-    finite = np.isfinite(y)
-    m = np.where(finite, mag, 0.0)
-    # neighbours: table[lo] <= m < table[lo + 1] (m <= 480 here)
-    hi = np.clip(np.searchsorted(table, m, side="right"), 1, 127)
-    lo = hi - 1
-    d_lo = m - table[lo]
-    d_hi = table[hi] - m
-    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (lo % 2 == 1))
+    nan = np.isnan(y)
+    m = np.where(nan, 0.0, np.abs(y))
+    if saturate:
+        m = np.minimum(m, 448.0)                       # also clamps +-inf
+    # neighbours table[lo] <= m < table[lo + 1], for m below 480
+    with np.errstate(invalid="ignore"):
+        hi = np.clip(np.searchsorted(table, m, side="right"), 1, 127)
+        lo = hi - 1
+        d_lo = m - table[lo]
+        d_hi = table[hi] - m
+        take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (lo % 2 == 1))
     code = np.where(take_hi, hi, lo).astype(np.uint8)
-    code = np.where(m > 480.0, np.uint8(0x7F), code)  # beyond the table: NaN
-    code = np.where(finite, code, np.uint8(0x7F))     # NaN, +-inf: NaN
+    code = np.where(m > 480.0, np.uint8(0x7F), code)  # beyond the table, inf: NaN
+    code = np.where(nan, np.uint8(0x7F), code)
     return (code | sign).astype(np.uint8)
 
 
@@ -70,14 +77,14 @@ def bf16_bits_to_f32(bits) -> np.ndarray:
 
 
 def scatter_ref(pool: np.ndarray, src_bits: np.ndarray, slots: np.ndarray,
-                inv_scale: float) -> np.ndarray:
+                inv_scale: float, saturate: bool = False) -> np.ndarray:
     """Copy of ``pool`` (uint8 [num_slots, W]) with row ``slots[r]`` replaced
     by the E4M3FN encoding of float32(src[r, :]) * float32(inv_scale)."""
     pool = np.array(pool, dtype=np.uint8, copy=True)
     src = bf16_bits_to_f32(src_bits)
     with np.errstate(invalid="ignore", over="ignore"):   # NaN / overflow inputs are expected
         y = (src * np.float32(inv_scale)).astype(np.float32)
-    codes = encode_e4m3fn(y)
+    codes = encode_e4m3fn(y, saturate)
     for r, s in enumerate(np.asarray(slots, dtype=np.int64)):
         if 0 <= s < pool.shape[0]:
             pool[s] = codes[r]

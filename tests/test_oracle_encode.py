@@ -27,9 +27,9 @@ def _bf16_bits(text):
     return bits >> 16
 
 
-def _golden_cases():
+def _golden_cases(name="e4m3_encode_rounding.txt"):
     rows = []
-    with open(os.path.join(GOLDEN, "e4m3_encode_rounding.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             line = line.split("#", 1)[0].strip()
             if line:
@@ -38,10 +38,10 @@ def _golden_cases():
     return rows
 
 
-def _golden_mismatches(encode):
+def _golden_mismatches(encode, name="e4m3_encode_rounding.txt", **kw):
     bad = []
-    for text, bits, code in _golden_cases():
-        got = int(encode(oracle.encode.bf16_bits_to_f32(np.uint16(bits))))
+    for text, bits, code in _golden_cases(name):
+        got = int(encode(oracle.encode.bf16_bits_to_f32(np.uint16(bits)), **kw))
         if got != code:
             bad.append((text, hex(code), hex(got)))
     return bad
@@ -50,6 +50,11 @@ def _golden_mismatches(encode):
 def test_golden_rounding_boundaries():
     assert len(_golden_cases()) >= 25
     assert _golden_mismatches(oracle.encode_e4m3fn) == []
+
+
+def test_golden_saturating_mode():
+    assert len(_golden_cases("e4m3_encode_saturate.txt")) >= 12
+    assert _golden_mismatches(oracle.encode_e4m3fn, "e4m3_encode_saturate.txt", saturate=True) == []
 
 
 def _torch_codes_of_bf16(bits_u16):
@@ -61,6 +66,15 @@ def test_all_bf16_patterns_match_torch_copy():
     bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
     ours = oracle.encode_e4m3fn(oracle.encode.bf16_bits_to_f32(bits))
     ref = _torch_codes_of_bf16(bits)
+    assert np.array_equal(ours, ref), np.nonzero(ours != ref)[0][:10]
+
+
+def test_all_bf16_patterns_saturating_match_torch_clamp_then_copy():
+    """Saturating mode = clamp to [-448, 448] (NaN passes through), then copy."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.encode_e4m3fn(oracle.encode.bf16_bits_to_f32(bits), saturate=True)
+    t = torch.from_numpy(bits.astype(np.int32)).to(torch.int16).view(torch.bfloat16).float()
+    ref = t.clamp(-448.0, 448.0).to(F8).view(torch.uint8).numpy()
     assert np.array_equal(ours, ref), np.nonzero(ours != ref)[0][:10]
 
 
@@ -120,6 +134,12 @@ def test_scatter_writes_only_named_slots():
     src = rng.integers(0, 1 << 16, size=(6, 576)).astype(np.uint16)
     slots = np.array([7, 0, 39, -1, 40, 12])      # -1 and 40 are outside the pool
     out = oracle.scatter_ref(pool, src, slots, 0.5)
+    sat = oracle.scatter_ref(pool, src, slots, 0.5, saturate=True)
+    with np.errstate(invalid="ignore"):
+        big = np.abs(oracle.encode.bf16_bits_to_f32(src[[0, 1, 2, 5]])) * np.float32(0.5) > 464
+    assert big.sum() > 100
+    assert np.all(sat[[7, 0, 39, 12]][big] & 0x7F == 0x7E)
+    assert np.array_equal(sat[[7, 0, 39, 12]][~big], out[[7, 0, 39, 12]][~big])
     with np.errstate(invalid="ignore"):
         y = (oracle.encode.bf16_bits_to_f32(src) * np.float32(0.5)).astype(np.float32)
     for r, s in enumerate(slots):
@@ -140,12 +160,16 @@ _MUTANTS = {
     "truncate": [("take_hi = (d_hi < d_lo)", "take_hi = (d_hi < -1.0)")],
     "saturate_overflow": [("v[0x7F] = 480.0", "v[0x7F] = 1e30"),
                           ("np.where(m > 480.0, np.uint8(0x7F), code)", "np.where(m > 448.0, np.uint8(0x7E), code)")],
-    "inf_saturates": [("code = np.where(finite, code, np.uint8(0x7F))",
-                       "code = np.where(finite, code, np.where(np.isnan(y), np.uint8(0x7F), np.uint8(0x7E)))")],
+    "inf_saturates": [("np.where(m > 480.0, np.uint8(0x7F), code)",
+                       "np.where(np.isinf(m), np.uint8(0x7E), np.where(m > 480.0, np.uint8(0x7F), code))")],
     "sign_dropped": [("return (code | sign)", "return (code)")],
     "neighbour_off_by_one": [("lo = hi - 1", "lo = np.maximum(hi - 2, 0)")],
-    "flush_subnormals": [("m = np.where(finite, mag, 0.0)", "m = np.where(finite & (mag >= 2.0**-6), mag, 0.0)")],
+    "flush_subnormals": [("m = np.where(nan, 0.0, np.abs(y))", "m = np.where(nan | (np.abs(y) < 2.0**-6), 0.0, np.abs(y))")],
+    "saturate_ignored": [("        m = np.minimum(m, 448.0)", "        pass")],
+    "saturate_clamps_nan": [("code = np.where(nan, np.uint8(0x7F), code)", "code = np.where(nan, np.uint8(0x7F if not saturate else 0x7E), code)")],
 }
+
+_SATURATE_MUTANTS = {"saturate_ignored", "saturate_clamps_nan"}
 
 
 def _mutant_encoder(name):
@@ -162,4 +186,8 @@ def _mutant_encoder(name):
 
 @pytest.mark.parametrize("name", sorted(_MUTANTS))
 def test_planted_mistakes_fail_the_golden_pins(name):
-    assert _golden_mismatches(_mutant_encoder(name)) != []
+    if name in _SATURATE_MUTANTS:
+        bad = _golden_mismatches(_mutant_encoder(name), "e4m3_encode_saturate.txt", saturate=True)
+    else:
+        bad = _golden_mismatches(_mutant_encoder(name))
+    assert bad != []
