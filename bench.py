@@ -1,6 +1,8 @@
 """Benchmark of the fused FP8 MLA decode (libfp8mla.so) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--replicas R]
+    python bench.py --config 3 [--layers 78]     (the pages' cast-path comparison)
+    python bench.py --write                      (the BF16 -> FP8 write path)
 
 A step is one fused decode call over one batch: mla_decode_fp8 on the batch-40
 workload (B=40 requests, 16 query heads sharing one 576-wide FP8 KV head,
@@ -44,6 +46,8 @@ def parse_args():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--write", action="store_true",
+                    help="time the BF16 -> FP8 write path (scatter_cast_bf16_fp8) instead")
     return ap.parse_args()
 
 
@@ -135,6 +139,9 @@ def main():
 
     if args.config == 3:
         print(json.dumps(cast_path_step(fm, workloads, torch, dev, args)), flush=True)
+        return
+    if args.write:
+        print(json.dumps(write_path(fm, workloads, torch, dev)), flush=True)
         return
 
     base = workloads.config(args.config, 0, device=dev)
@@ -306,6 +313,89 @@ def cast_path_step(fm, workloads, torch, dev, args):
         "fused_speedup_vs_cast_then_attend": round(cast_path_ms / fused_ms, 1),
         "fused_speedup_vs_gather_then_attend": round(gather_path_ms / fused_ms, 2),
     }
+
+
+def write_path(fm, workloads, torch, dev, sizes=(40, 1024, 16384, 65536)):
+    """The write path into one layer's 495,552-slot FP8 pool: n new BF16 rows
+    quantised and scattered to distinct random slots, for a decode step's 40
+    rows and extend chunks.  Sources rotate over >= 256 MB so reads come from
+    HBM.  Bytes moved per row: 1152 read + 576 written + 4 slot id.
+
+    `us` is device time per call: the calls are captured once in a HIP graph
+    and the graph is replayed, so host launch cost is excluded (the kernel
+    allocates and clears nothing, so it captures as is).  `us_eager` is the
+    same loop launched from Python, for small n bound by the host.  The pages'
+    own path (a BF16 -> FP8 copy, then an index write, two kernels plus a
+    temporary) is timed eagerly beside it."""
+    stream = torch.cuda.current_stream(dev)
+    pool = workloads.random_pool(495552, seed=4242, device=dev)
+    res = {"metric": "BF16 -> FP8 write path: quantise + scatter into a 495,552-slot pool",
+           "unit": "us/call, GB/s", "higher_is_better": False, "data": "synthetic",
+           "dtype": "bf16 -> fp8_e4m3fn", "bytes_per_row": 1152 + 576 + 4, "sizes": {}}
+    for n in sizes:
+        R = min(64, max(2, -(-256 * 2 ** 20 // (n * 1152))))
+        srcs = [workloads.new_kv_rows(n, seed=50 + r, device=dev) for r in range(R)]
+        slots = [torch.from_numpy(workloads.free_slots(n, 495552, seed=90 + r)).to(dev)
+                 for r in range(R)]
+        longs = [s.long() for s in slots]
+        iters = max(20, min(2000, int(2e6 // n)))
+
+        def ours(i):
+            fm.scatter_cast_bf16_fp8(srcs[i], slots[i], pool)
+
+        def pages_path(i):
+            pool[longs[i]] = srcs[i].to(torch.float8_e4m3fn).view(torch.uint8)
+
+        def eager_us(fn):
+            for i in range(min(R, 10)):
+                fn(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize(dev)
+            e0.record(stream)
+            for i in range(iters):
+                fn(i % R)
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            return e0.elapsed_time(e1) * 1e3 / iters
+
+        def graph_us(fn, calls):
+            side = torch.cuda.Stream(device=dev)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for i in range(3):
+                    fn(i % R)
+            stream.wait_stream(side)
+            torch.cuda.synchronize(dev)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(calls):
+                    fn(i % R)
+            g.replay()
+            torch.cuda.synchronize(dev)
+            best = None
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize(dev)
+                t = e0.elapsed_time(e1) * 1e3 / calls
+                best = t if best is None else min(best, t)
+            del g
+            return best
+
+        us = graph_us(ours, max(R, min(400, iters)))
+        us_e = eager_us(ours)
+        us_t = eager_us(pages_path)
+        moved = n * (1152 + 576 + 4)
+        res["sizes"][str(n)] = {
+            "us": round(us, 2), "GBps": round(moved / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100 * moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 1),
+            "us_eager": round(us_e, 2),
+            "torch_copy_then_index_us_eager": round(us_t, 2),
+            "speedup_eager_vs_torch_path": round(us_t / us_e, 2)}
+        del srcs, slots, longs
+    return res
 
 
 def secondary(fm, reps, outs, wss, stream, dev, args):

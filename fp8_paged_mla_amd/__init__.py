@@ -1,5 +1,6 @@
 """Python binding of libfp8mla.so: MLA decode over a paged FP8-E4M3FN latent KV
-cache, plus the full-pool and gather-then-cast FP8->BF16 casts, for MI355X.
+cache, the full-pool and gather-then-cast FP8->BF16 casts, and the BF16->FP8
+write path into the cache, for MI355X.
 
 Argument marshalling only.  Every step of the computation runs in the HIP
 kernels of ``libfp8mla.so``; PyTorch provides device memory and the current
@@ -11,7 +12,8 @@ The operations follow three public write-ups on FP8 KV caches for MLA models:
 ``[495552, 1, 576]`` Float8_e4m3fn pool and the native-FP8 attention that
 replaces it), "The Gather-Then-Cast Pivot" (gathering only the active rows
 before casting) and "When a Faster Kernel Doesn't Speed Up Serving" (the
-CastFromFP8 history cast on the extend path).
+CastFromFP8 history cast on the extend path and the CastToFP8 write of new KV
+rows into the FP8 cache).
 """
 import ctypes
 import os
@@ -29,6 +31,7 @@ __all__ = [
     "library",
     "cast_pool_fp8_bf16",
     "gather_cast_fp8_bf16",
+    "scatter_cast_bf16_fp8",
     "mla_decode_fp8",
     "mla_decode_fp8_workspace_bytes",
     "mla_decode_bf16",
@@ -63,6 +66,8 @@ def library() -> ctypes.CDLL:
     lib.cast_pool_fp8_bf16.restype = ctypes.c_int
     lib.gather_cast_fp8_bf16.argtypes = [vp, i64, vp, i64, vp, vp]
     lib.gather_cast_fp8_bf16.restype = ctypes.c_int
+    lib.scatter_cast_bf16_fp8.argtypes = [vp, i64, i64, vp, vp, i64, f32, i32, vp]
+    lib.scatter_cast_bf16_fp8.restype = ctypes.c_int
     lib.mla_decode_fp8.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, f32, f32, vp, vp, sz, vp]
     lib.mla_decode_fp8.restype = ctypes.c_int
     lib.mla_decode_fp8_workspace_bytes.argtypes = [i32, i32, i64]
@@ -160,6 +165,41 @@ def gather_cast_fp8_bf16(pool: torch.Tensor, indices: torch.Tensor,
                                               out.data_ptr(), _stream_handle(dev)),
                "gather_cast_fp8_bf16")
     return out
+
+
+def scatter_cast_bf16_fp8(src: torch.Tensor, slots: torch.Tensor, pool: torch.Tensor,
+                          inv_scale: float = 1.0, saturate: bool = False) -> torch.Tensor:
+    """Write path: ``pool[slots[r], :] = e4m3fn(float32(src[r, :]) * inv_scale)``, in place.
+
+    src [n, 576] (or [n, 1, 576]) bf16 whose rows may be strided (last dim
+    contiguous, row stride a multiple of 8); slots [n] int32, distinct; pool
+    [num_slots, 576] E4M3FN bytes.  Rows whose slot is outside the pool are
+    skipped.  ``saturate`` clamps overflow to +-448 instead of giving NaN.
+    Returns ``pool``.
+    """
+    pool_rows = _pool_rows(pool)
+    _require(pool_rows, "pool")
+    dev = pool_rows.device
+    if not isinstance(src, torch.Tensor) or src.device != dev or src.dtype != torch.bfloat16:
+        raise TypeError("src must be a bfloat16 tensor on %s" % dev)
+    if src.dim() == 3 and src.shape[1] == 1:
+        src = src[:, 0, :]
+    if src.dim() != 2 or src.shape[1] != KV_WIDTH:
+        raise ValueError("src must be [n, 576] (or [n, 1, 576]), got %s" % (tuple(src.shape),))
+    n = src.shape[0]
+    row_stride = src.stride(0) if n > 1 else max(src.stride(0), KV_WIDTH)
+    if src.stride(1) != 1:
+        raise ValueError("src rows must be contiguous")
+    _require(slots, "slots", torch.int32, dev)
+    if slots.dim() != 1 or slots.shape[0] != n:
+        raise ValueError("slots must be [%d]" % n)
+    with torch.cuda.device(dev):
+        _check(library().scatter_cast_bf16_fp8(src.data_ptr(), n, row_stride, slots.data_ptr(),
+                                               pool_rows.data_ptr(), pool_rows.shape[0],
+                                               float(inv_scale), 1 if saturate else 0,
+                                               _stream_handle(dev)),
+               "scatter_cast_bf16_fp8")
+    return pool
 
 
 def mla_decode_fp8_workspace_bytes(batch: int, num_heads: int, total_tokens: int,

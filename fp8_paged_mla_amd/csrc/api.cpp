@@ -50,7 +50,7 @@ const char* fp8mla_status_string(int status) {
     case FP8MLA_ERR_BAD_SHAPE: return "invalid size argument";
     case FP8MLA_ERR_MISALIGNED: return "tensor pointer not 16-byte aligned";
     case FP8MLA_ERR_WORKSPACE: return "workspace missing or too small";
-    case FP8MLA_ERR_BAD_SCALAR: return "scale must be finite and > 0, sm_scale finite";
+    case FP8MLA_ERR_BAD_SCALAR: return "scale / inv_scale must be finite and > 0, sm_scale finite";
     case FP8MLA_ERR_HIP: return "HIP runtime error or kernel launch failure";
     default: return "unknown status";
   }
@@ -78,6 +78,28 @@ int gather_cast_fp8_bf16(const uint8_t* pool, int64_t num_slots, const int32_t* 
   if (!aligned16(pool) || !aligned16(out) || !aligned4(indices)) return FP8MLA_ERR_MISALIGNED;
   const hipError_t e = fp8mla::launch_gather_cast(pool, num_slots, indices, n, out,
                                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
+}
+
+int scatter_cast_bf16_fp8(const uint16_t* src, int64_t n, int64_t src_row_stride,
+                          const int32_t* slots, uint8_t* pool, int64_t num_slots,
+                          float inv_scale, int32_t saturate, void* stream) {
+  if (n < 0 || n > kMaxTokens || num_slots < 0 || num_slots > kMaxSlots)
+    return FP8MLA_ERR_BAD_SHAPE;
+  if (src_row_stride < FP8MLA_KV_WIDTH || src_row_stride % 8 != 0 ||
+      src_row_stride > (int64_t)1 << 40)
+    return FP8MLA_ERR_BAD_SHAPE;
+  if (!isfinite(inv_scale) || !(inv_scale > 0.0f)) return FP8MLA_ERR_BAD_SCALAR;
+  if (n == 0) return FP8MLA_OK;
+  if (num_slots == 0) return FP8MLA_ERR_BAD_SHAPE;
+  if (!src || !slots || !pool) return FP8MLA_ERR_NULL_PTR;
+  if (!aligned16(src) || !aligned16(pool) || !aligned4(slots)) return FP8MLA_ERR_MISALIGNED;
+  // int32 slot ids name at most INT32_MAX slots; negative ids then compare as
+  // unsigned values past the last slot and are skipped.
+  const int64_t writable = num_slots < (int64_t)INT32_MAX ? num_slots : (int64_t)INT32_MAX;
+  const hipError_t e = fp8mla::launch_scatter_cast(src, src_row_stride, n, slots, pool, writable,
+                                                   inv_scale, saturate != 0,
+                                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
 }
 

@@ -14,6 +14,10 @@ hipError_t launch_cast_pool(const uint8_t* pool, int64_t num_slots, uint16_t* ou
 hipError_t launch_gather_cast(const uint8_t* pool, int64_t num_slots, const int32_t* indices,
                               int64_t n, uint16_t* out, hipStream_t stream);
 
+hipError_t launch_scatter_cast(const uint16_t* src, int64_t src_row_stride, int64_t n,
+                               const int32_t* slots, uint8_t* pool, int64_t num_slots,
+                               float inv_scale, bool saturate, hipStream_t stream);
+
 // Decode schedule: equal segments of the request-tile list x head groups, and the split-K
 // workspace layout (per-request piece ranges, partial outputs, log2-sum-exp values).
 // Which split kernel a decode call runs: FP8 rows with 16 heads per

@@ -1,6 +1,7 @@
 /*
  * fp8mla.h -- C ABI of libfp8mla.so: MLA decode attention that reads a paged
- * FP8-E4M3FN latent KV cache directly, plus the two cast paths it replaces.
+ * FP8-E4M3FN latent KV cache directly, the two cast paths it replaces, and
+ * the write path that quantises new BF16 KV rows into the cache.
  * Hand-written HIP kernels for gfx950 (MI355X).
  *
  * Source of the operations (the pages are three public write-ups):
@@ -14,8 +15,9 @@
  *    Assumptions: gather only the active FP8 rows into a compact buffer, cast
  *    that, and run BF16 attention over sequential indices.
  *  - "When a Faster Kernel Doesn't Speed Up Serving: Profiling FP8 KV Cache
- *    on AMD Instinct MI308X" (ROCm blog), Step 3 (CastFromFP8): the same
- *    FP8->BF16 history cast on the extend path.
+ *    on AMD Instinct MI308X" (ROCm blog), Step 3: CastFromFP8, the same
+ *    FP8->BF16 history cast on the extend path, and CastToFP8, the BF16->FP8
+ *    copy that writes new KV rows into the cache.
  *
  * Conventions for every call:
  *  - All tensor arguments are DEVICE pointers on the current HIP device,
@@ -31,8 +33,9 @@
  *    argument returns a negative status and launches nothing.  There is no
  *    silent fallback to another path.
  *  - Slot indices are the caller's contract (0 <= index < num_slots).  The
- *    kernels clamp every index into the pool, so an out-of-range index gives
- *    a wrong row, never an out-of-bounds access.
+ *    reading kernels clamp every index into the pool, so an out-of-range
+ *    index gives a wrong row, never an out-of-bounds access; the writing
+ *    kernel (scatter_cast_bf16_fp8) skips rows whose slot is out of range.
  */
 #ifndef FP8MLA_H
 #define FP8MLA_H
@@ -54,7 +57,7 @@ extern "C" {
 #define FP8MLA_ERR_BAD_SHAPE (-2)       /* a size is negative, zero where not allowed, or too large */
 #define FP8MLA_ERR_MISALIGNED (-3)      /* a tensor pointer is not 16-byte aligned         */
 #define FP8MLA_ERR_WORKSPACE (-4)       /* workspace NULL or smaller than required         */
-#define FP8MLA_ERR_BAD_SCALAR (-5)      /* scale or sm_scale not finite, or scale <= 0     */
+#define FP8MLA_ERR_BAD_SCALAR (-5)      /* a scale not finite, or scale / inv_scale <= 0   */
 #define FP8MLA_ERR_HIP (-6)             /* a HIP runtime call or kernel launch failed      */
 
 /*
@@ -86,6 +89,41 @@ int cast_pool_fp8_bf16(const uint8_t* pool, int64_t num_slots, uint16_t* out, vo
  */
 int gather_cast_fp8_bf16(const uint8_t* pool, int64_t num_slots, const int32_t* indices,
                          int64_t n, uint16_t* out, void* stream);
+
+/*
+ * scatter_cast_bf16_fp8 -- the write path into the FP8 cache
+ * ("When a Faster Kernel Doesn't Speed Up Serving", Step 3, CastToFP8:
+ * set_kv_buffer stores freshly computed BF16 KV rows into the FP8 KV cache
+ * through a BF16 -> Float8_e4m3fn copy).
+ *
+ *   pool[slots[r], j] = e4m3fn(float32(src[r, j]) * inv_scale)
+ *                                       for 0 <= r < n, 0 <= j < 576
+ *
+ * The product is rounded to float32 first, then to the nearest E4M3FN value,
+ * ties to the even code.  saturate == 0 is the copy's rule (torch's float ->
+ * Float8_e4m3fn): magnitudes above 464, the midpoint between 448 and the next
+ * step up, and infinities give NaN (0x7F / 0xFF); 464 itself gives 448.
+ * saturate != 0 clamps magnitudes to 448 first, so overflow and infinities
+ * give +-448 (0x7E / 0xFE).  In both modes NaN gives NaN, the sign bit is
+ * kept (-0 -> 0x80), and 2^-9 multiples below 2^-6 are subnormal codes.
+ * inv_scale = 1 is the pages' unscaled copy; a per-tensor dequant scale s
+ * of the read path pairs with inv_scale = 1 / s.
+ *   src       uint16 [n, src_row_stride] BF16, read; element (r, j) at
+ *                                       src[r * src_row_stride + j], j < 576
+ *   n >= 0 (0 is a no-op)
+ *   src_row_stride >= 576, a multiple of 8 (elements)
+ *   slots     int32  [n]                destination slot of each row
+ *   pool      uint8  [num_slots, 576]   written in place, rows slots[r] only;
+ *                                       every other byte is left unchanged
+ *   num_slots >= 1 when n > 0
+ *   inv_scale finite and > 0, else FP8MLA_ERR_BAD_SCALAR
+ * Rows whose slot is negative or >= num_slots are not written.  Slots must
+ * be distinct; with duplicates the bytes of a slot come from any one of its
+ * rows, chunk by chunk.  src must not overlap pool.
+ */
+int scatter_cast_bf16_fp8(const uint16_t* src, int64_t n, int64_t src_row_stride,
+                          const int32_t* slots, uint8_t* pool, int64_t num_slots,
+                          float inv_scale, int32_t saturate, void* stream);
 
 /*
  * mla_decode_fp8 -- fused MLA decode over the paged FP8 latent cache

@@ -92,6 +92,36 @@ def test_gather_cast_validation():
     assert lib.gather_cast_fp8_bf16(P16, 10, P16, 3, P8, NULL) == ERR_ALIGN
 
 
+def test_scatter_cast_validation():
+    lib = _lib()
+
+    def sc(**kw):
+        a = dict(src=P16, n=3, stride=576, slots=P16, pool=P16, num_slots=10, inv=1.0, sat=0,
+                 stream=NULL)
+        a.update(kw)
+        return lib.scatter_cast_bf16_fp8(a["src"], a["n"], a["stride"], a["slots"], a["pool"],
+                                         a["num_slots"], a["inv"], a["sat"], a["stream"])
+
+    assert sc(n=-1) == ERR_SHAPE
+    assert sc(n=1 << 31) == ERR_SHAPE
+    assert sc(num_slots=-1) == ERR_SHAPE
+    assert sc(num_slots=0) == ERR_SHAPE
+    assert sc(stride=575) == ERR_SHAPE
+    assert sc(stride=580) == ERR_SHAPE            # not a multiple of 8 elements
+    assert sc(inv=0.0) == ERR_SCALAR
+    assert sc(inv=-2.0) == ERR_SCALAR
+    assert sc(inv=math.inf) == ERR_SCALAR
+    assert sc(inv=math.nan) == ERR_SCALAR
+    assert sc(n=0) == 0                           # no-op, nothing launched
+    assert sc(n=0, src=NULL, slots=NULL, pool=NULL, num_slots=0) == 0
+    assert sc(src=NULL) == ERR_NULL
+    assert sc(slots=NULL) == ERR_NULL
+    assert sc(pool=NULL) == ERR_NULL
+    assert sc(src=P8) == ERR_ALIGN
+    assert sc(pool=P8) == ERR_ALIGN
+    assert sc(slots=P16 + 2) == ERR_ALIGN
+
+
 def _decode(lib, **kw):
     a = dict(q=P16, pool=P16, slots=100, indptr=P16, indices=P16, total=10, B=2, H=16,
              scale=1.0, sm=0.07, out=P16, ws=P16, ws_bytes=1 << 20, stream=NULL)
@@ -166,3 +196,6 @@ def test_binding_rejects_cpu_tensors():
     pool = torch.zeros((4, 576), dtype=torch.uint8)
     with pytest.raises(ValueError):
         fm.cast_pool_fp8_bf16(pool)
+    with pytest.raises(ValueError):
+        fm.scatter_cast_bf16_fp8(torch.zeros((2, 576), dtype=torch.bfloat16),
+                                 torch.zeros(2, dtype=torch.int32), pool)

@@ -104,6 +104,30 @@ def random_q(B: int, H: int, seed: int, device="cpu", sigma: float = 1.0) -> tor
     return q.to(torch.bfloat16)
 
 
+def new_kv_rows(n: int, seed: int, device="cpu", sigma: float = 1.0,
+                outlier_frac: float = 0.0) -> torch.Tensor:
+    """bfloat16 [n, 576]: freshly computed KV rows for the write path, N(0, sigma^2),
+    with a fraction of elements replaced by magnitudes U[400, 600] (random sign)
+    that straddle the E4M3FN range."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed + 104729)
+    x = torch.randn((n, KV_WIDTH), generator=g, device=device, dtype=torch.float32)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    if outlier_frac > 0.0:
+        u = torch.rand((n, KV_WIDTH), generator=g, device=device)
+        mag = 400.0 + 200.0 * torch.rand((n, KV_WIDTH), generator=g, device=device)
+        sgn = torch.where(torch.rand((n, KV_WIDTH), generator=g, device=device) < 0.5, -1.0, 1.0)
+        x = torch.where(u < outlier_frac, sgn * mag, x)
+    return x.to(torch.bfloat16)
+
+
+def free_slots(n: int, num_slots: int, seed: int) -> np.ndarray:
+    """int32 [n]: n distinct destination slots drawn at random from the pool."""
+    rng = np.random.default_rng(seed)
+    return rng.choice(num_slots, size=n, replace=False).astype(np.int32)
+
+
 def assign_slots(lengths, num_slots: int, page_size: int, rng) -> np.ndarray:
     """Concatenated slot ids for requests of the given lengths.
 
