@@ -3,6 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--replicas R]
     python bench.py --config 3 [--layers 78]     (the pages' cast-path comparison)
     python bench.py --write                      (the BF16 -> FP8 write path)
+    python bench.py --serving-step {bf16,fp8_cast,fp8_fused} [--layers L] [--trace T.json]
+                                                 (one decode step over L layers: KV write +
+                                                  attention, for the paired-trace ledger)
 
 A step is one fused decode call over one batch: mla_decode_fp8 on the batch-40
 workload (B=40 requests, 16 query heads sharing one 576-wide FP8 KV head,
@@ -46,6 +49,10 @@ def parse_args():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--serving-step", choices=["bf16", "fp8_cast", "fp8_fused"], default=None,
+                    help="time one decode step (KV write + attention per layer) of a KV-cache variant")
+    ap.add_argument("--trace", default=None,
+                    help="with --serving-step: torch-profiler trace (chrome JSON) of the timed steps")
     ap.add_argument("--write", action="store_true",
                     help="time the BF16 -> FP8 write path (scatter_cast_bf16_fp8) instead")
     return ap.parse_args()
@@ -142,6 +149,9 @@ def main():
         return
     if args.write:
         print(json.dumps(write_path(fm, workloads, torch, dev)), flush=True)
+        return
+    if args.serving_step:
+        print(json.dumps(serving_step(fm, workloads, torch, dev, args)), flush=True)
         return
 
     base = workloads.config(args.config, 0, device=dev)
@@ -313,6 +323,93 @@ def cast_path_step(fm, workloads, torch, dev, args):
         "fused_speedup_vs_cast_then_attend": round(cast_path_ms / fused_ms, 1),
         "fused_speedup_vs_gather_then_attend": round(gather_path_ms / fused_ms, 2),
     }
+
+
+def serving_step(fm, workloads, torch, dev, args):
+    """One decode step of the batch-40 workload over `layers` layers, each with its
+    own 495,552-slot pool: per layer, the step's 40 new KV rows are written to
+    their requests' newest slots, then attention runs over every request's
+    history.  Three KV-cache variants of the same step, as in the pages' paired
+    traces ("When a Faster Kernel Doesn't Speed Up Serving", Step 1; "The KV
+    Cache Cast Bottleneck", The Context):
+      bf16      -- BF16 pools: index write, attention over BF16 rows;
+      fp8_cast  -- FP8 pools, the pages' path: BF16 -> FP8 copy + index write,
+                   full-pool FP8 -> BF16 copy, attention over the BF16 copy;
+      fp8_fused -- FP8 pools: scatter_cast_bf16_fp8, mla_decode_fp8.
+    With --trace, the timed steps are recorded with the torch profiler (kernel
+    names and durations for fp8_paged_mla_amd.ledger)."""
+    L = args.layers
+    K = max(1, min(args.steps, 20))
+    w = workloads.config(2, 0, device=dev)
+    pools8 = [w.pool] + [workloads.random_pool(495552, seed=2000 + 7 * l + 1, device=dev)
+                         for l in range(1, L)]
+    newest = (w.indptr[1:] - 1).long()
+    slots = w.indices[newest].contiguous()
+    slots_l = slots.long()
+    rows = [workloads.new_kv_rows(w.B, seed=7000 + l, device=dev) for l in range(L)]
+    out = torch.empty((w.B, w.H, 512), dtype=torch.bfloat16, device=dev)
+    variant = args.serving_step
+    if variant == "bf16":
+        pools16 = [fm.cast_pool_fp8_bf16(p) for p in pools8]
+        del pools8
+        ws = torch.empty(max(256, fm.mla_decode_bf16_workspace_bytes(w.B, w.H, w.total_tokens)),
+                         dtype=torch.uint8, device=dev)
+
+        def layer(l):
+            pools16[l][slots_l] = rows[l]
+            fm.mla_decode_bf16(w.q, pools16[l], w.indptr, w.indices, w.scale, w.sm_scale,
+                               out=out, workspace=ws)
+    elif variant == "fp8_cast":
+        cast_out = torch.empty((495552, 576), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(256, fm.mla_decode_bf16_workspace_bytes(w.B, w.H, w.total_tokens)),
+                         dtype=torch.uint8, device=dev)
+
+        def layer(l):
+            pools8[l][slots_l] = rows[l].to(torch.float8_e4m3fn).view(torch.uint8)
+            cast_out.copy_(pools8[l].view(torch.float8_e4m3fn))
+            fm.mla_decode_bf16(w.q, cast_out, w.indptr, w.indices, w.scale, w.sm_scale,
+                               out=out, workspace=ws)
+    else:
+        ws = torch.empty(max(256, fm.mla_decode_fp8_workspace_bytes(w.B, w.H, w.total_tokens)),
+                         dtype=torch.uint8, device=dev)
+
+        def layer(l):
+            fm.scatter_cast_bf16_fp8(rows[l], slots, pools8[l])
+            fm.mla_decode_fp8(w.q, pools8[l], w.indptr, w.indices, w.scale, w.sm_scale,
+                              out=out, workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def steps(k):
+        for _ in range(k):
+            for l in range(L):
+                layer(l)
+
+    steps(2)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    steps(K)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / K
+    res = {"metric": "decode step over %d layers: KV write + attention, %s KV cache" % (L, variant),
+           "value": round(ms, 4), "unit": "ms/step", "higher_is_better": False,
+           "steps": K, "data": "synthetic",
+           "config": {"workload": workloads.CONFIG_NAMES[2], "layers": L, "variant": variant}}
+    if args.trace:
+        from torch.profiler import ProfilerActivity, profile
+        with profile(activities=[ProfilerActivity.CPU, ProfilerActivity.CUDA],
+                     record_shapes=True) as prof:
+            steps(K)
+            torch.cuda.synchronize(dev)
+        prof.export_chrome_trace(args.trace)
+        from fp8_paged_mla_amd import ledger
+        t = ledger.totals_from_kernels(ledger.read_kernel_events(args.trace))
+        res["trace"] = args.trace
+        res["categories_ms_per_step"] = {c: round(v[1] / K, 4) for c, v in t.rows.items()}
+        res["kernels_per_step"] = {c: v[0] / K for c, v in t.rows.items()}
+    return res
 
 
 def write_path(fm, workloads, torch, dev, sizes=(40, 1024, 16384, 65536)):
