@@ -24,6 +24,10 @@ What it computes, and where the pages define it:
   576 dims, values from the first 512 ("The KV Cache Cast Bottleneck",
   *The Context*; "The Gather-Then-Cast Pivot", *The Subject Message*), with a
   max-subtracted softmax, in float64.
+* ``extend``: the same attention with several new query tokens per request
+  and a causal mask over the request's cache list, the extend/prefill path
+  ("When a Faster Kernel Doesn't Speed Up Serving", *Step 3*, CastFromFP8;
+  "The KV Cache Cast Bottleneck", *The Message*).
 
 Pinned by the ``-m "not gpu"`` tests (OCP special values, torch's own FP8
 decode, brute force, closed forms and invariants).  The attention numerics at
@@ -33,6 +37,7 @@ those pins.
 from .e4m3 import decode_table, e4m3fn_value, bf16_bits_of, cast_table_bf16
 from .encode import encode_e4m3fn, scatter_ref
 from .cast import cast_ref, gather_ref
+from .extend import mla_extend_ref, visible_tokens
 from .attention import (
     bf16_bits_to_f64,
     mla_decode_ref,
@@ -53,6 +58,8 @@ __all__ = [
     "scatter_ref",
     "bf16_bits_to_f64",
     "mla_decode_ref",
+    "mla_extend_ref",
+    "visible_tokens",
     "mla_decode_partial_ref",
     "combine_partials_ref",
     "KV_WIDTH",
