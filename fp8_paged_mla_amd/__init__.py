@@ -7,6 +7,9 @@ kernels of ``libfp8mla.so``; PyTorch provides device memory and the current
 stream.  There is no fallback: if the library is missing or a call fails, an
 exception is raised.
 
+The extend (prefill) attention ``mla_extend_fp8`` serves several new query
+tokens per request with a causal mask.
+
 The operations follow three public write-ups on FP8 KV caches for MLA models:
 "The KV Cache Cast Bottleneck" (the full-pool ``.to()`` cast of a
 ``[495552, 1, 576]`` Float8_e4m3fn pool and the native-FP8 attention that
@@ -35,6 +38,8 @@ __all__ = [
     "mla_decode_fp8",
     "mla_decode_fp8_workspace_bytes",
     "mla_decode_bf16",
+    "mla_extend_fp8",
+    "mla_extend_fp8_workspace_bytes",
     "mla_decode_bf16_workspace_bytes",
     "status_string",
     "KV_WIDTH",
@@ -72,6 +77,11 @@ def library() -> ctypes.CDLL:
     lib.mla_decode_fp8.restype = ctypes.c_int
     lib.mla_decode_fp8_workspace_bytes.argtypes = [i32, i32, i64]
     lib.mla_decode_fp8_workspace_bytes.restype = sz
+    lib.mla_extend_fp8.argtypes = [vp, vp, i64, vp, vp, vp, i64, i64, i32, i32, f32, f32, i32,
+                                   vp, vp, sz, vp]
+    lib.mla_extend_fp8.restype = ctypes.c_int
+    lib.mla_extend_fp8_workspace_bytes.argtypes = [i32, i32, i64]
+    lib.mla_extend_fp8_workspace_bytes.restype = sz
     lib.mla_decode_bf16.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, f32, f32, vp, vp, sz, vp]
     lib.mla_decode_bf16.restype = ctypes.c_int
     lib.mla_decode_bf16_workspace_bytes.argtypes = [i32, i32, i64]
@@ -200,6 +210,63 @@ def scatter_cast_bf16_fp8(src: torch.Tensor, slots: torch.Tensor, pool: torch.Te
                                                _stream_handle(dev)),
                "scatter_cast_bf16_fp8")
     return pool
+
+
+def mla_extend_fp8_workspace_bytes(batch: int, num_heads: int, total_q: int, device=None) -> int:
+    """Bytes of workspace mla_extend_fp8 needs (scratch; no initialisation)."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        return int(library().mla_extend_fp8_workspace_bytes(int(batch), int(num_heads), int(total_q)))
+
+
+def mla_extend_fp8(q: torch.Tensor, kv_pool: torch.Tensor, qo_indptr: torch.Tensor,
+                   kv_indptr: torch.Tensor, kv_indices: torch.Tensor, scale: float,
+                   sm_scale: float, causal: bool = True, out: torch.Tensor = None,
+                   workspace: torch.Tensor = None) -> torch.Tensor:
+    """Extend (prefill) attention reading the FP8 pool directly.
+
+    q [total_q, H, 576] bf16 (request b's new tokens are rows
+    qo_indptr[b]:qo_indptr[b+1]); kv_pool [num_slots, 576] E4M3FN;
+    qo_indptr, kv_indptr [B+1] int32; kv_indices int32 slot ids (the last
+    q_len_b entries of request b's list are its new tokens).  With ``causal``
+    token i of request b sees the first kv_len_b - q_len_b + i + 1 tokens.
+    Returns out [total_q, H, 512] bf16.
+    """
+    kv_pool = _pool_rows(kv_pool)
+    _require(q, "q", torch.bfloat16)
+    dev = q.device
+    _require(kv_pool, "kv_pool", None, dev)
+    _require(qo_indptr, "qo_indptr", torch.int32, dev)
+    _require(kv_indptr, "kv_indptr", torch.int32, dev)
+    _require(kv_indices, "kv_indices", torch.int32, dev)
+    if q.dim() != 3 or q.shape[2] != KV_WIDTH:
+        raise ValueError("q must be [total_q, H, 576], got %s" % (tuple(q.shape),))
+    total_q, H = q.shape[0], q.shape[1]
+    if qo_indptr.dim() != 1 or kv_indptr.dim() != 1 or qo_indptr.shape != kv_indptr.shape:
+        raise ValueError("qo_indptr and kv_indptr must both be [B+1]")
+    B = qo_indptr.shape[0] - 1
+    if B < 1:
+        raise ValueError("need at least one request")
+    if kv_indices.dim() != 1:
+        raise ValueError("kv_indices must be 1-D")
+    if out is None:
+        out = torch.empty((total_q, H, V_WIDTH), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev)
+    if tuple(out.shape) != (total_q, H, V_WIDTH):
+        raise ValueError("out must be [%d, %d, 512]" % (total_q, H))
+    need = mla_extend_fp8_workspace_bytes(B, H, total_q, dev)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _require(workspace, "workspace", torch.uint8, dev)
+    with torch.cuda.device(dev):
+        _check(library().mla_extend_fp8(q.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
+                                        qo_indptr.data_ptr(), kv_indptr.data_ptr(),
+                                        kv_indices.data_ptr(), total_q, kv_indices.shape[0], B, H,
+                                        float(scale), float(sm_scale), 1 if causal else 0,
+                                        out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                        _stream_handle(dev)),
+               "mla_extend_fp8")
+    return out
 
 
 def mla_decode_fp8_workspace_bytes(batch: int, num_heads: int, total_tokens: int,

@@ -19,7 +19,7 @@ LIB_NAME = "libfp8mla.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "cast.hip", "scatter_cast.hip", "mla_decode.hip", "mla_decode_h64.hip", "mla_decode_bf16.hip"]
+SOURCES = ["api.cpp", "cast.hip", "scatter_cast.hip", "mla_decode.hip", "mla_decode_h64.hip", "mla_decode_bf16.hip", "mla_extend.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -103,6 +103,45 @@ int scatter_cast_bf16_fp8(const uint16_t* src, int64_t n, int64_t src_row_stride
   return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
 }
 
+size_t mla_extend_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_q) {
+  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_q < 0 ||
+      total_q >= fp8mla::kExtendMaxQueryRows || batch > INT32_MAX / 2)
+    return 0;
+  if (total_q == 0) return 0;
+  const int cus = current_device_cus();
+  if (cus <= 0) return 0;
+  return fp8mla::plan_mla_extend(batch, num_heads, total_q, cus).workspace_bytes;
+}
+
+int mla_extend_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                   const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                   int64_t total_q, int64_t total_kv, int32_t batch, int32_t num_heads,
+                   float scale, float sm_scale, int32_t causal, uint16_t* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (batch < 1 || batch > INT32_MAX / 2 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS ||
+      total_q < 0 || total_q >= fp8mla::kExtendMaxQueryRows || total_kv < 0 ||
+      total_kv > kMaxTokens || num_slots < 0 || num_slots > kMaxSlots)
+    return FP8MLA_ERR_BAD_SHAPE;
+  if (total_kv > 0 && num_slots == 0) return FP8MLA_ERR_BAD_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.0f) || !isfinite(sm_scale)) return FP8MLA_ERR_BAD_SCALAR;
+  if (total_q == 0) return FP8MLA_OK;
+  if (!q || !qo_indptr || !kv_indptr || !out || !workspace) return FP8MLA_ERR_NULL_PTR;
+  if (total_kv > 0 && (!kv_pool || !kv_indices)) return FP8MLA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(out) || !aligned4(qo_indptr) || !aligned4(kv_indptr) ||
+      !aligned16(workspace))
+    return FP8MLA_ERR_MISALIGNED;
+  if (total_kv > 0 && (!aligned16(kv_pool) || !aligned4(kv_indices))) return FP8MLA_ERR_MISALIGNED;
+  const int cus = current_device_cus();
+  if (cus <= 0) return FP8MLA_ERR_HIP;
+  const fp8mla::ExtendPlan plan = fp8mla::plan_mla_extend(batch, num_heads, total_q, cus);
+  if (workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
+  const hipError_t e = fp8mla::launch_mla_extend(q, kv_pool, num_slots, qo_indptr, kv_indptr,
+                                                 kv_indices, total_q, total_kv, batch, num_heads,
+                                                 scale, sm_scale, causal != 0, out, workspace,
+                                                 plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
+}
+
 size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens) {
   if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_tokens < 0 ||
       total_tokens > kMaxTokens)

@@ -34,7 +34,19 @@ struct SplitParams {
   int32_t xcd_per;
   float score_scale;  // sm_scale * scale * log2(e): scores in the base-2 domain
   float kv_scale;
+  // Extend (several query tokens per request) only.  The kernels then walk
+  // virtual requests, one per (request, block of query tokens), built on the
+  // device: indptr is their CSR of visible-token counts (padded with empty
+  // requests up to B), and per virtual request vinfo holds (offset from a CSR
+  // position to its kv_indices entry, first query row | (tokens in the block
+  // - 1) << 29).
+  const int2* vinfo;
+  int32_t rows_per_tok;  // query rows per token (heads rounded up to 16) if <= 64, else 0
+  int32_t causal;
 };
+
+constexpr int kExtQ0Bits = 29;                 // first query row in the low 29 bits of vinfo.y
+constexpr int kExtQ0Mask = (1 << kExtQ0Bits) - 1;
 
 __device__ __forceinline__ float wave_max_over_groups(float x) {
   // lanes h, h+16, h+32, h+48 hold the same head
@@ -100,7 +112,7 @@ struct SegmentSpan {
 // (64 per step); every wave computes the same result.  Segment 0 also writes
 // the zero outputs (and piece records) of requests without tokens, for its
 // WG_HEADS heads (head set hg).  Returns false if the segment holds no tile.
-template <int SHIFT, int THREADS, int WG_HEADS = HEADS>
+template <int SHIFT, int THREADS, int WG_HEADS = HEADS, bool ZERO_EMPTY = true>
 __device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int hg, int lane,
                                              SegmentSpan& sp) {
   const int N = p.total_tokens;
@@ -113,6 +125,7 @@ __device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int 
       const int b = c + __builtin_ctzll(empty);
       empty &= empty - 1;
       if (hg == 0 && threadIdx.x == 0 && p.req_pieces) p.req_pieces[b] = make_int2(0, 0);
+      if (!ZERO_EMPTY) continue;  // the caller's combine writes those rows
       for (int i = threadIdx.x; i < WG_HEADS * 64; i += THREADS) {
         const int h = hg * WG_HEADS + (i >> 6);
         if (h < p.H)
@@ -167,8 +180,21 @@ __device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int 
 // Walks the tiles of consecutive requests: request b, tile j of its nt
 // tiles, request range [lo, hi).  Requests without tokens are skipped.  The
 // kv_indptr values come from a 64-entry window held one entry per lane.
-template <int SHIFT>
-struct TileCursor {
+// With EXT the requests are virtual (see SplitParams) and the cursor also
+// carries the current one's index offset and query rows (from a window of
+// vinfo held the same way).
+template <bool EXT>
+struct CursorExtFields {};  // decode: no extra fields (the cursor must stay in registers)
+template <>
+struct CursorExtFields<true> {
+  int delta, q0n;            // vinfo of the current virtual request
+  int win_delta, win_q0n;    // vinfo window, one entry per lane
+  __device__ __forceinline__ int q_row0() const { return q0n & kExtQ0Mask; }
+  __device__ __forceinline__ int q_tokens() const { return (q0n >> kExtQ0Bits) + 1; }
+};
+
+template <int SHIFT, bool EXT = false>
+struct TileCursor : CursorExtFields<EXT> {
   int b, j, nt, lo, hi;
   int win, win_val;
   __device__ __forceinline__ int tile_lo() const { return lo + (j << SHIFT); }
@@ -177,6 +203,11 @@ struct TileCursor {
   __device__ __forceinline__ void load_window(const SplitParams& p, int first, int lane) {
     win = first;
     win_val = clamp_tok(p.indptr[min(first + lane, p.B)], p.total_tokens);
+    if constexpr (EXT) {
+      const int2 vi = p.vinfo[min(first + lane, p.B - 1)];
+      this->win_delta = vi.x;
+      this->win_q0n = vi.y;
+    }
   }
   // (every field assigned exactly once on every path, so that the cursor
   // stays in registers)
@@ -189,6 +220,10 @@ struct TileCursor {
     lo = valid ? l : 0;
     hi = valid ? h : 0;
     nt = valid ? (h - l + (1 << SHIFT) - 1) >> SHIFT : 0;
+    if constexpr (EXT) {
+      this->delta = valid ? __builtin_amdgcn_readlane(this->win_delta, nb - win) : 0;
+      this->q0n = valid ? __builtin_amdgcn_readlane(this->win_q0n, nb - win) : 0;
+    }
   }
   __device__ __forceinline__ void start(const SplitParams& p, int b0, int j0, int lane) {
     load_window(p, b0, lane);
@@ -277,12 +312,15 @@ __device__ __forceinline__ void merge_pieces(const uint16_t* part_o, const float
     for (int off = 1; off < 8; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
     const float m_new = fmaxf(M, __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
                                      __builtin_bit_cast(int, cm))));
-    const float r = __builtin_amdgcn_exp2f(M - m_new);  // 0 on the first chunk
+    // pieces without tokens (lse -inf) weigh nothing; while every piece so
+    // far is empty, subtract 0 instead of -inf
+    const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+    const float r = __builtin_amdgcn_exp2f(M - m_sub);  // 0 on the first chunk
     den *= r;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= r;
     M = m_new;
-    const float wl = lane < cnt ? __builtin_amdgcn_exp2f(lv - M) : 0.f;
+    const float wl = lane < cnt ? __builtin_amdgcn_exp2f(lv - m_sub) : 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (u < cnt) {
@@ -295,7 +333,7 @@ __device__ __forceinline__ void merge_pieces(const uint16_t* part_o, const float
       }
     }
   }
-  const float inv = kv_scale / den;
+  const float inv = den > 0.f ? kv_scale / den : 0.f;  // no token at all: a zero row
   uint4 v;
   v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);

@@ -1,4 +1,4 @@
-// Host-side pieces shared by the two decode translation units (internal).
+// Host-side pieces shared by the decode and extend translation units (internal).
 #pragma once
 
 #include "decode_common.h"
@@ -15,5 +15,8 @@ decode::SplitParams make_split_params(const uint16_t* q, const void* kv_rows, in
 // Merge of the partials of requests spanning several segments (one wave per
 // request and head).
 hipError_t launch_mla_combine(const decode::SplitParams& sp, hipStream_t stream);
+
+// The 64-row split kernel in its extend form (virtual requests, causal limits).
+hipError_t launch_mla_split_h64_extend(const decode::SplitParams& sp, int grid, hipStream_t stream);
 
 }  // namespace fp8mla

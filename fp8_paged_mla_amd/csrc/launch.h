@@ -75,6 +75,44 @@ hipError_t launch_mla_decode_h64(const uint16_t* q, const uint8_t* kv_pool, int6
                                  float scale, float sm_scale, uint16_t* out, void* workspace,
                                  const DecodePlan& plan, hipStream_t stream);
 
+// Extend: several query tokens per request, causal or not.  The 64-row
+// kernel runs over virtual requests -- a request and a block of T of its
+// query tokens -- that a one-workgroup pre-pass builds on the device from
+// qo_indptr and kv_indptr, so the host never reads either.  Rows of a
+// workgroup are (token, head) pairs: T = 64 / rows_per_tok tokens of
+// rows_per_tok rows (heads rounded up to 16) when that is at most 64, else
+// one token and HG sets of 64 heads.
+struct ExtendPlan {
+  int32_t rows_per_tok;   // 0 when heads > 64
+  int32_t tokens_per_wg;  // T
+  int32_t HG;
+  int32_t Hp;             // partial-result rows per virtual request (64 * HG)
+  int32_t vmax;           // bound on the virtual requests: batch + ceil(total_q / T)
+  int32_t nseg;
+  int32_t items;
+  int32_t xcd_per;
+  int32_t grid;
+  size_t vstart_offset;   // int32 [batch + 1]: first virtual request of each request
+  size_t vindptr_offset;  // int32 [vmax + 1]: CSR of visible-token counts
+  size_t vinfo_offset;    // int2 [vmax]
+  size_t pieces_offset;   // int2 [vmax]: (segment of the first piece, pieces)
+  size_t part_o_offset;   // fp16 [(nseg + vmax) * Hp * 512]
+  size_t lse_offset;      // float [(nseg + vmax) * Hp]
+  size_t workspace_bytes; // also holds the header {virtual requests, CSR total} at offset 0
+};
+
+constexpr int64_t kExtendMaxQueryRows = (int64_t)1 << 29;   // first query row packs into 29 bits
+constexpr int64_t kExtendMaxVirtualTokens = (int64_t)1 << 29;  // CSR total the split can address
+
+ExtendPlan plan_mla_extend(int32_t batch, int32_t num_heads, int64_t total_q, int num_cus);
+
+hipError_t launch_mla_extend(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                             const int32_t* qo_indptr, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, int64_t total_q, int64_t total_kv,
+                             int32_t batch, int32_t num_heads, float scale, float sm_scale,
+                             bool causal, uint16_t* out, void* workspace, const ExtendPlan& plan,
+                             hipStream_t stream);
+
 constexpr int kFp8TileTokens = 128;
 constexpr int kH64TileTokens = 64;
 constexpr int kBf16TileTokens = 64;

@@ -470,7 +470,7 @@ decode::SplitParams make_split_params(const uint16_t* q, const void* kv_rows, in
                                       float scale, float sm_scale, uint16_t* out,
                                       void* workspace, const DecodePlan& pl) {
   char* ws = reinterpret_cast<char*>(workspace);
-  decode::SplitParams sp;
+  decode::SplitParams sp{};
   sp.q = q;
   sp.pool = reinterpret_cast<const uint8_t*>(kv_rows);
   sp.indptr = kv_indptr;

@@ -19,6 +19,13 @@
 // Rows are copied global -> LDS (global_load_lds) into three slots of 64
 // rows: tile k+2 goes into the slot of tile k-1 once every wave has finished
 // tile k-1's value reads (the first barrier of tile k), ~1.5 tiles ahead.
+//
+// The extend instantiation (EXT) serves several query tokens per request:
+// the 64 rows of a workgroup are (token, head) pairs of one virtual request
+// (a request and a block of its query tokens, built on the device), so every
+// KV tile is shared by the block's tokens as it is by the heads.  A wave's 16
+// rows belong to one token, whose causal limit masks the scores; a token
+// without visible tokens in a piece yields an empty partial (lse -inf).
 #include "decode_host.h"
 
 namespace fp8mla {
@@ -99,6 +106,7 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
 // LDS banks.
 __device__ __forceinline__ int tile_row(int B, int m) { return 16 * B + ((B & 1) ? (m ^ 12) : m); }
 
+template <bool EXT>
 __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSLOTS * TILE_BYTES];
   __shared__ float mx_lds[NWAVES][HEADS];
@@ -118,14 +126,25 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   if (item >= p.items) return;
   const int seg = item / p.HG;
   const int hs = item - seg * p.HG;
-  const int head = hs * WG_HEADS + hgl * HEADS + t;
+  // row: this lane's row of the workgroup's partial results; decode: the
+  // head.  Extend: rows are (token tk of the block, head), 16-row groups never
+  // straddle tokens (rows per token is a multiple of 16), so tk is per wave.
+  const int row = hs * WG_HEADS + hgl * HEADS + t;
+  int head = row, tk = 0;
+  if constexpr (EXT) {
+    if (p.rows_per_tok > 0) {
+      tk = (hgl * HEADS) / p.rows_per_tok;
+      head = hgl * HEADS - tk * p.rows_per_tok + t;
+    }
+  }
 
   SegmentSpan span;
-  if (!find_segment<TILE_SHIFT, THREADS, WG_HEADS>(p, seg, hs, lane, span)) return;
+  if (!find_segment<TILE_SHIFT, THREADS, WG_HEADS, !EXT>(p, seg, hs, lane, span)) return;
   const int ntiles = span.ntiles;
-  TileCursor<TILE_SHIFT> cc;
+  using Cursor = TileCursor<TILE_SHIFT, EXT>;
+  Cursor cc;
   cc.start(p, span.b0, span.j0, lane);
-  TileCursor<TILE_SHIFT> lc = cc;
+  Cursor lc = cc;
 
   auto opaque_lane = [&]() -> int {
     int l = lane;
@@ -137,7 +156,9 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   auto load_next_index = [&]() -> int32_t {
     const int tlo = lc.tile_lo();
     const int tok = tlo + ROWS_PER_WAVE * w + (t & 7);
-    const int32_t* a = lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) : p.indices;
+    int off = 0;  // extend: CSR position -> kv_indices entry
+    if constexpr (EXT) off = lc.delta;
+    const int32_t* a = lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) + off : p.indices;
     const int32_t v = issue_load_i32(a);
     lc.advance(p, lane);
     return v;
@@ -164,13 +185,20 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
 
   // query of this wave's head group, in the d-order of the K reads: step
   // s = 2i + e, lane (t, g): q[head t][64i + 16g + 8e .. +8]
-  auto q_lane_ptr = [&](int b) -> const uint16_t* {
-    return p.q + ((int64_t)b * p.H + min(head, p.H - 1)) * KV_WIDTH + 16 * g;
+  auto q_lane_ptr = [&](const Cursor& c) -> const uint16_t* {
+    int64_t qrow = c.b;
+    if constexpr (EXT) qrow = c.q_row0() + min(tk, c.q_tokens() - 1);
+    return p.q + (qrow * p.H + min(head, p.H - 1)) * KV_WIDTH + 16 * g;
+  };
+  // rows without a query (heads past H; extend: tokens past the block) keep a zero query
+  auto row_idle = [&]() -> bool {
+    if constexpr (EXT) return head >= p.H || tk >= cc.q_tokens();
+    return head >= p.H;
   };
   bf16x8_t qr[QSTEPS];
   auto finish_q = [&]() {
     pin_q(qr);
-    if (head >= p.H) {
+    if (row_idle()) {
 #pragma unroll
       for (int s = 0; s < QSTEPS; ++s) qr[s] = bf16x8_t{};
     }
@@ -183,7 +211,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   wait_vm<0>();
   pin(ixA);
   pin(ixB);
-  issue_load_q(qr, q_lane_ptr(cc.b));
+  issue_load_q(qr, q_lane_ptr(cc));
   issue_tile(0, ixA);
   ixA = load_next_index();
   if (ntiles > 1) issue_tile(1, ixB);
@@ -224,23 +252,27 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     const float l = l_lds[hgl][t] + l_lds[hgl + 4][t];
     // lane (t, g) holds columns 256 half + 16c + 4g + 0..3 of its head
     if (complete) {
-      if (head < p.H) {
-        const float inv = p.kv_scale / l;
-        uint16_t* op = p.out + ((int64_t)cc.b * p.H + head) * V_WIDTH + 256 * half + 4 * g;
+      if (!row_idle()) {
+        int64_t orow = cc.b;
+        if constexpr (EXT) orow = cc.q_row0() + tk;
+        // extend: a token with no visible token gets a zero row
+        const float inv = EXT && l == 0.f ? 0.f : p.kv_scale / l;
+        uint16_t* op = p.out + (orow * p.H + head) * V_WIDTH + 256 * half + 4 * g;
 #pragma unroll
         for (int c = 0; c < VBLOCKS; ++c)
           *reinterpret_cast<uint2*>(op + 16 * c) =
               make_uint2(pack_bf16x2(O[c][0] * inv, O[c][1] * inv), pack_bf16x2(O[c][2] * inv, O[c][3] * inv));
       }
     } else {
-      const int64_t piece = (int64_t)(seg + cc.b) * p.Hp + head;
-      const float inv = 1.0f / l;
+      const int64_t piece = (int64_t)(seg + cc.b) * p.Hp + row;
+      const bool empty = EXT && l == 0.f;  // extend: no visible token in this piece
+      const float inv = empty ? 0.f : 1.0f / l;
       uint16_t* op = p.part_o + piece * V_WIDTH + 256 * half + 4 * g;
 #pragma unroll
       for (int c = 0; c < VBLOCKS; ++c)
         *reinterpret_cast<uint2*>(op + 16 * c) =
             make_uint2(pack_f16x2(O[c][0] * inv, O[c][1] * inv), pack_f16x2(O[c][2] * inv, O[c][3] * inv));
-      if (half == 0 && g == 0) p.part_lse[piece] = m_run + __builtin_amdgcn_logf(l);
+      if (half == 0 && g == 0) p.part_lse[piece] = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l);
     }
 #pragma unroll
     for (int c = 0; c < VBLOCKS; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -256,7 +288,12 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   int slot_k = 0;  // k % 3
   auto process_tile = [&](int k, int32_t& ix_cur, int32_t& ix_next) {
     const int tile_lo = cc.tile_lo();
-    const int tile_hi = cc.tile_hi();
+    int tile_hi = cc.tile_hi();
+    if constexpr (EXT) {  // this wave's token sees the first lim tokens of the request
+      const int len = cc.hi - cc.lo;
+      const int lim = p.causal ? len - (cc.q_tokens() - 1 - tk) : len;
+      tile_hi = min(tile_hi, cc.lo + max(lim, 0));
+    }
     const bool last_of_request = cc.j + 1 == cc.nt;
     const uint8_t* slot = kv_lds + slot_k * TILE_BYTES;
     const int slot_next2 = slot_k == 0 ? 2 : slot_k - 1;  // (k + 2) % 3
@@ -294,16 +331,18 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     pin(ix_cur);
     ix_next = load_next_index();
     const bool new_q = last_of_request && k + 1 < ntiles;
-    TileCursor<TILE_SHIFT> nc = cc;
+    Cursor nc = cc;
     if (new_q) {
       nc.advance(p, lane);
-      issue_load_q(qr, q_lane_ptr(nc.b));
+      issue_load_q(qr, q_lane_ptr(nc));
     }
     if (k + 2 < ntiles) issue_tile(slot_next2, ix_cur);
 
     const float tmax = fmaxf(mx_lds[hgl][t], mx_lds[hgl + 4][t]);
     const float m_new = fmaxf(m_run, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // extend: while a token has seen nothing (m -inf), subtract 0 instead
+    const float m_sub = EXT && m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
     if (__ballot(alpha != 1.0f)) {
 #pragma unroll
       for (int c = 0; c < VBLOCKS; ++c) O[c] *= alpha;
@@ -313,8 +352,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     float pr0[4], pr1[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pr0[r] = __builtin_amdgcn_exp2f(s0[r] - m_new);
-      pr1[r] = __builtin_amdgcn_exp2f(s1[r] - m_new);
+      pr0[r] = __builtin_amdgcn_exp2f(s0[r] - m_sub);
+      pr1[r] = __builtin_amdgcn_exp2f(s1[r] - m_sub);
     }
     const uint32_t p01 = pack_bf16x2(pr0[0], pr0[1]), p23 = pack_bf16x2(pr0[2], pr0[3]);
     const uint32_t q01 = pack_bf16x2(pr1[0], pr1[1]), q23 = pack_bf16x2(pr1[2], pr1[3]);
@@ -377,10 +416,15 @@ hipError_t launch_mla_decode_h64(const uint16_t* q, const uint8_t* kv_pool, int6
   const decode::SplitParams sp = make_split_params(q, kv_pool, num_slots, kv_indptr, kv_indices,
                                                    total_tokens, batch, num_heads, scale,
                                                    sm_scale, out, workspace, pl);
-  hipLaunchKernelGGL(mla_split_h64_kernel, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
+  hipLaunchKernelGGL(mla_split_h64_kernel<false>, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || total_tokens == 0) return e;
   return launch_mla_combine(sp, stream);
+}
+
+hipError_t launch_mla_split_h64_extend(const decode::SplitParams& sp, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_split_h64_kernel<true>, dim3(grid), dim3(THREADS), 0, stream, sp);
+  return hipGetLastError();
 }
 
 }  // namespace fp8mla

@@ -198,6 +198,55 @@ int mla_decode_bf16(const uint16_t* q, const uint16_t* kv, int64_t num_rows,
 /* Workspace size in bytes for mla_decode_bf16 (as mla_decode_fp8_workspace_bytes). */
 size_t mla_decode_bf16_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens);
 
+/*
+ * mla_extend_fp8 -- extend (prefill) MLA attention reading the paged FP8 cache
+ * directly ("When a Faster Kernel Doesn't Speed Up Serving", Step 3,
+ * CastFromFP8: on every extend step the prefill attention reads each
+ * request's whole KV history, which the original stack casts to BF16 first;
+ * "The KV Cache Cast Bottleneck", The Message: the direct-FP8 MLA wrapper on
+ * the extend path as well).
+ *
+ * Request b has the query rows qo_indptr[b] .. qo_indptr[b+1]-1 (q_len_b new
+ * tokens) and the cache tokens kv_indices[kv_indptr[b] .. kv_indptr[b+1]-1]
+ * (kv_len_b, the new tokens' own KV being the last q_len_b of them, written
+ * before the call).  Query token i of request b sees the first n_i of them:
+ *   causal != 0:  n_i = clamp(kv_len_b - q_len_b + i + 1, 0, kv_len_b)
+ *   causal == 0:  n_i = kv_len_b
+ * and, with K[t,:] = scale * e4m3fn(kv_pool[slot_t, :]) over those n_i tokens,
+ *   out[qo_indptr[b] + i, h, :] = sum_t softmax_t(sm_scale * <q[qo_indptr[b] + i, h, :], K[t, :]>) * K[t, 0:512]
+ * (BF16, round-to-nearest-even); n_i = 0 gives a zero row.  One token per
+ * request (q_len_b = 1) is the decode of mla_decode_fp8.
+ *   q           uint16 [total_q, num_heads, 576]   BF16, read
+ *   kv_pool     uint8  [num_slots, 576]            E4M3FN bytes, read
+ *   qo_indptr   int32  [batch + 1]  0 = qo_indptr[0] <= ... <= qo_indptr[batch] <= total_q
+ *   kv_indptr   int32  [batch + 1]  0 = kv_indptr[0] <= ... <= kv_indptr[batch] <= total_kv
+ *   kv_indices  int32  [total_kv]   slot ids in [0, num_slots)
+ *   out         uint16 [total_q, num_heads, 512]   BF16, written (rows of
+ *                                     requests in the indptr ranges only)
+ *   workspace   at least mla_extend_fp8_workspace_bytes(batch, num_heads,
+ *               total_q) bytes of scratch (no initialisation needed,
+ *               garbage afterwards; NULL allowed when total_q == 0)
+ *   1 <= batch, 1 <= num_heads <= FP8MLA_MAX_HEADS, 0 <= total_q < 2^29,
+ *   0 <= total_kv <= 2^31 - 1; num_slots >= 1 when total_kv > 0;
+ *   scale finite > 0, sm_scale finite.
+ * The index arrays are read on the device only.  Out-of-range indptr
+ * entries are clamped into [0, total_q] / [0, total_kv] (a wrong row, never
+ * an out-of-bounds access).  Per call, at most 2^29 (token block, visible
+ * token) pairs -- sum over blocks of 4 (H <= 16), 2 (H <= 32) or 1 query
+ * tokens of the block's last limit -- are supported; beyond that the call
+ * leaves out unwritten.
+ */
+int mla_extend_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                   const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                   int64_t total_q, int64_t total_kv, int32_t batch, int32_t num_heads,
+                   float scale, float sm_scale, int32_t causal, uint16_t* out, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Workspace size in bytes for mla_extend_fp8 (0 when total_q == 0 or on bad
+ * arguments); depends on batch, num_heads, total_q and the device's compute
+ * unit count. */
+size_t mla_extend_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_q);
+
 /* Static description of a status code; never NULL. */
 const char* fp8mla_status_string(int status);
 

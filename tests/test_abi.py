@@ -199,3 +199,41 @@ def test_binding_rejects_cpu_tensors():
     with pytest.raises(ValueError):
         fm.scatter_cast_bf16_fp8(torch.zeros((2, 576), dtype=torch.bfloat16),
                                  torch.zeros(2, dtype=torch.int32), pool)
+
+
+def test_mla_extend_validation():
+    lib = _lib()
+
+    def ext(**kw):
+        a = dict(q=P16, pool=P16, slots=100, qo=P16, kv=P16, idx=P16, tq=10, tkv=40, B=2, H=16,
+                 scale=1.0, sm=0.07, causal=1, out=P16, ws=P16, ws_bytes=1 << 30, stream=NULL)
+        a.update(kw)
+        return lib.mla_extend_fp8(a["q"], a["pool"], a["slots"], a["qo"], a["kv"], a["idx"],
+                                  a["tq"], a["tkv"], a["B"], a["H"], a["scale"], a["sm"],
+                                  a["causal"], a["out"], a["ws"], a["ws_bytes"], a["stream"])
+
+    assert ext(B=0) == ERR_SHAPE
+    assert ext(H=0) == ERR_SHAPE
+    assert ext(H=257) == ERR_SHAPE
+    assert ext(tq=-1) == ERR_SHAPE
+    assert ext(tq=1 << 29) == ERR_SHAPE
+    assert ext(tkv=-1) == ERR_SHAPE
+    assert ext(tkv=1 << 31) == ERR_SHAPE
+    assert ext(slots=0) == ERR_SHAPE
+    assert ext(scale=0.0) == ERR_SCALAR
+    assert ext(sm=math.nan) == ERR_SCALAR
+    assert ext(tq=0) == 0                              # no query rows: no-op
+    assert ext(q=NULL) == ERR_NULL
+    assert ext(qo=NULL) == ERR_NULL
+    assert ext(kv=NULL) == ERR_NULL
+    assert ext(out=NULL) == ERR_NULL
+    assert ext(ws=NULL) == ERR_NULL
+    assert ext(pool=NULL) == ERR_NULL
+    assert ext(idx=NULL) == ERR_NULL
+    assert ext(q=P8) == ERR_ALIGN
+    assert ext(out=P8) == ERR_ALIGN
+    assert ext(qo=P16 + 2) == ERR_ALIGN
+    assert ext(ws=P8) == ERR_ALIGN
+    assert lib.mla_extend_fp8_workspace_bytes(0, 16, 10) == 0
+    assert lib.mla_extend_fp8_workspace_bytes(1, 16, 0) == 0
+    assert lib.mla_extend_fp8_workspace_bytes(1, 300, 10) == 0

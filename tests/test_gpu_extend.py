@@ -1,0 +1,135 @@
+"""GPU parity of the extend (prefill) attention mla_extend_fp8 against the
+float64 oracle: several query tokens per request, causal or not, ragged
+token counts, head counts on both sides of 64, blocks spanning segments,
+tokens that see nothing, and the named extend workloads (sampled rows)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import assert_attention_close, bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+fm = pytest.importorskip("fp8_paged_mla_amd")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _args(w):
+    return (bf16_bits(w.q), w.pool.cpu().numpy(), w.qo_indptr.cpu().numpy(),
+            w.kv_indptr.cpu().numpy(), w.kv_indices.cpu().numpy(), w.scale, w.sm_scale)
+
+
+def _run(w, dev, **kw):
+    out = fm.mla_extend_fp8(w.q.to(dev), w.pool.to(dev), w.qo_indptr.to(dev), w.kv_indptr.to(dev),
+                            w.kv_indices.to(dev), w.scale, w.sm_scale, causal=w.causal, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(w, dev, label="", rows=None):
+    print("case:", label, w.name, "q_lens", w.q_lens.tolist()[:8], "kv_lens", w.kv_lens.tolist()[:8],
+          flush=True)
+    got = _run(w, dev)
+    ref = oracle.mla_extend_ref(*_args(w), causal=w.causal, rows=rows)
+    g = got if rows is None else got[torch.as_tensor(rows, device=got.device)]
+    return assert_attention_close(g, ref, label)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("H", [16, 8, 32, 48, 64, 128])
+def test_head_counts(dev, H, causal):
+    w = workloads.extend(3, H, [5, 1, 9], [40, 200, 3], seed=H, causal=causal, scale=1.5)
+    _check(w, dev, "H=%d causal=%s" % (H, causal))
+
+
+@pytest.mark.parametrize("q_lens,history", [
+    ([1], [0]),                          # one token, no history
+    ([2, 3, 4, 5], [0, 1, 63, 64]),      # ragged blocks around the 4-token block size
+    ([7, 0, 13], [100, 50, 129]),        # a request without query tokens
+    ([64], [0]),                         # prefill from scratch
+    ([33, 17], [500, 1000]),
+])
+def test_ragged_blocks(dev, q_lens, history):
+    w = workloads.extend(len(q_lens), 16, q_lens, history, seed=len(q_lens) + sum(q_lens))
+    _check(w, dev, "ragged %s/%s" % (q_lens, history))
+
+
+def test_one_token_per_request_matches_decode(dev):
+    w = workloads.extend(6, 16, [1] * 6, [300, 1, 2000, 77, 64, 640], seed=11, scale=0.75)
+    got = _run(w, dev)
+    ref = oracle.mla_extend_ref(*_args(w))
+    assert_attention_close(got, ref, "q_len 1")
+    dec = fm.mla_decode_fp8(w.q.to(dev), w.pool.to(dev), w.kv_indptr.to(dev), w.kv_indices.to(dev),
+                            w.scale, w.sm_scale)
+    torch.cuda.synchronize()
+    assert_attention_close(dec, ref, "decode")
+
+
+def test_blocks_span_many_segments(dev):
+    """Enough tokens that virtual requests are cut across several segments,
+    so their partials go through the combine."""
+    w = workloads.extend(2, 16, [8, 6], [6000, 9000], seed=12)
+    _check(w, dev, "multi-segment")
+    w = workloads.extend(1, 128, [3], [7000], seed=13)
+    _check(w, dev, "multi-segment H=128")
+
+
+def test_tokens_that_see_nothing_get_zero_rows(dev):
+    # kv_len < q_len: the first tokens of request 0 see no cache token
+    w = workloads.extend(2, 16, [6, 2], [0, 5], seed=14)
+    kv = w.kv_lens.copy()
+    kv[0] = 3
+    w.kv_lens = kv
+    ind = np.concatenate([[0], np.cumsum(kv)])
+    w.kv_indptr = torch.from_numpy(ind.astype(np.int32))
+    w.kv_indices = w.kv_indices[: int(ind[-1])].contiguous()
+    e = _check(w, dev, "kv_len < q_len")
+    got = _run(w, dev).float().cpu()
+    assert torch.all(got[0:3] == 0)
+
+
+def test_no_cache_tokens_at_all(dev):
+    w = workloads.extend(2, 16, [3, 2], [0, 0], seed=15)
+    w.kv_lens = np.zeros(2, dtype=np.int64)
+    w.kv_indptr = torch.zeros(3, dtype=torch.int32)
+    w.kv_indices = torch.zeros(0, dtype=torch.int32)
+    got = _run(w, dev)
+    assert torch.all(got.float() == 0)
+
+
+def test_workspace_garbage_and_reuse(dev):
+    shapes = [([4, 9], [700, 30], 16), ([1, 1, 1], [5000, 2, 9], 16), ([12], [3000], 64)]
+    ws = torch.empty(1 << 27, dtype=torch.uint8, device=dev).random_(0, 256)
+    for rep in range(2):
+        for k, (ql, hist, H) in enumerate(shapes):
+            w = workloads.extend(len(ql), H, ql, hist, seed=20 + k)
+            need = fm.mla_extend_fp8_workspace_bytes(w.B, H, w.total_q)
+            assert need <= ws.numel()
+            got = fm.mla_extend_fp8(w.q.to(dev), w.pool.to(dev), w.qo_indptr.to(dev),
+                                    w.kv_indptr.to(dev), w.kv_indices.to(dev), w.scale, w.sm_scale,
+                                    workspace=ws)
+            torch.cuda.synchronize()
+            assert_attention_close(got, oracle.mla_extend_ref(*_args(w)), "reuse %d/%d" % (rep, k))
+
+
+def test_deterministic(dev):
+    w = workloads.extend(2, 32, [9, 4], [3000, 800], seed=30)
+    a = _run(w, dev)
+    b = _run(w, dev)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", list(workloads.EXTEND_NAMES))
+def test_named_extend_workloads_sampled(dev, name):
+    w = workloads.extend_config(name, device="cpu")
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, w.total_q - 1], rng.integers(0, w.total_q, size=12)]))
+    _check(w, dev, name, rows=rows)

@@ -224,3 +224,96 @@ def small(B, H, lengths, num_slots=None, page_size=1, seed=0, scale=1.0,
         num_slots = max(page_size, 2 * need + 3 * page_size)
     return build("custom B=%d H=%d" % (B, H), seed, B, H, lengths, num_slots, page_size,
                  scale, sm_scale, device=device, q_sigma=q_sigma, outlier_frac=outlier_frac)
+
+
+# ---------------------------------------------------------------- extend / prefill
+
+EXTEND_NAMES = {
+    "spec4": "extend spec4: B=40 H=16 q_len=4 history~U[1024,8192] page=1 pool=495552",
+    "chunk1k": "extend chunk1k: B=4 H=16 q_len=1024 history~U[2048,8192] page=1 pool=495552",
+    "prefill4k_h64": "extend prefill4k_h64: B=1 H=64 q_len=4096 history=0 page=1 pool=495552",
+}
+
+
+@dataclass
+class ExtendWorkload:
+    name: str
+    seed: int
+    B: int
+    H: int
+    q_lens: np.ndarray             # int64 [B] new query tokens per request
+    kv_lens: np.ndarray            # int64 [B] cache tokens per request (history + new)
+    num_slots: int
+    pool: torch.Tensor             # uint8 [num_slots, 576]
+    qo_indptr: torch.Tensor        # int32 [B+1]
+    kv_indptr: torch.Tensor        # int32 [B+1]
+    kv_indices: torch.Tensor       # int32 [sum(kv_lens)]; request b's new tokens are its last q_len
+    q: torch.Tensor                # bfloat16 [sum(q_lens), H, 576]
+    scale: float
+    sm_scale: float
+    causal: bool = True
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q_lens.sum())
+
+    def visible_tokens(self) -> int:
+        """Sum over query tokens of the cache tokens each sees."""
+        tot = 0
+        for ql, kl in zip(self.q_lens.tolist(), self.kv_lens.tolist()):
+            if self.causal:
+                i = np.arange(ql)
+                tot += int(np.clip(kl - ql + i + 1, 0, kl).sum())
+            else:
+                tot += ql * kl
+        return tot
+
+    def kv_bytes(self) -> int:
+        return KV_WIDTH * int(self.kv_lens.sum())
+
+
+def extend(B, H, q_lens, history, num_slots=None, page_size=1, seed=0, scale=1.0,
+           sm_scale=1.0 / math.sqrt(192.0), device="cpu", causal=True, q_sigma=1.0,
+           outlier_frac=0.0, name=None) -> ExtendWorkload:
+    """An extend batch: request b has history[b] cached tokens and q_lens[b] new
+    ones, whose KV is already in the cache as the last q_lens[b] entries of its
+    list.  Slots, pool values and queries are drawn as for decode."""
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    kv_lens = np.asarray(history, dtype=np.int64) + q_lens
+    rng = np.random.default_rng(seed)
+    if num_slots is None:
+        need = int(((kv_lens + page_size - 1) // page_size).sum()) * page_size
+        num_slots = max(page_size, 2 * need + 3 * page_size)
+    indices = assign_slots(kv_lens, num_slots, page_size, rng)
+    qo = np.zeros(B + 1, dtype=np.int64)
+    qo[1:] = np.cumsum(q_lens)
+    kv = np.zeros(B + 1, dtype=np.int64)
+    kv[1:] = np.cumsum(kv_lens)
+    pool = random_pool(num_slots, seed, device=device, outlier_frac=outlier_frac)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed + 7919)
+    q = torch.randn((int(qo[-1]), H, KV_WIDTH), generator=g, device=device, dtype=torch.float32)
+    if q_sigma != 1.0:
+        q.mul_(q_sigma)
+    to = lambda a: torch.from_numpy(np.asarray(a).astype(np.int32)).to(device)
+    return ExtendWorkload(name or "extend B=%d H=%d" % (B, H), seed, B, H, q_lens, kv_lens,
+                          num_slots, pool, to(qo), to(kv), to(indices), q.to(torch.bfloat16),
+                          float(scale), float(sm_scale), bool(causal))
+
+
+def extend_config(name: str, replica: int = 0, device="cpu") -> ExtendWorkload:
+    """One of the named extend workloads (see EXTEND_NAMES)."""
+    seed = 9000 + 100 * list(EXTEND_NAMES).index(name) + replica
+    rng = np.random.default_rng(seed)
+    if name == "spec4":
+        hist = rng.integers(1024, 8192, size=40, endpoint=True)
+        return extend(40, 16, [4] * 40, hist, 495552, seed=seed, device=device,
+                      name=EXTEND_NAMES[name])
+    if name == "chunk1k":
+        hist = rng.integers(2048, 8192, size=4, endpoint=True)
+        return extend(4, 16, [1024] * 4, hist, 495552, seed=seed, device=device,
+                      name=EXTEND_NAMES[name])
+    if name == "prefill4k_h64":
+        return extend(1, 64, [4096], [0], 495552, seed=seed, device=device,
+                      name=EXTEND_NAMES[name])
+    raise ValueError(name)
