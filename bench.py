@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--replicas R]
     python bench.py --config 3 [--layers 78]     (the pages' cast-path comparison)
     python bench.py --write                      (the BF16 -> FP8 write path)
+    python bench.py --extend {spec4,chunk1k,prefill4k_h64}   (extend / prefill attention)
     python bench.py --serving-step {bf16,fp8_cast,fp8_fused} [--layers L] [--trace T.json]
                                                  (one decode step over L layers: KV write +
                                                   attention, for the paired-trace ledger)
@@ -53,6 +54,9 @@ def parse_args():
                     help="time one decode step (KV write + attention per layer) of a KV-cache variant")
     ap.add_argument("--trace", default=None,
                     help="with --serving-step: torch-profiler trace (chrome JSON) of the timed steps")
+    ap.add_argument("--extend", default=None,
+                    choices=["spec4", "chunk1k", "prefill4k_h64"],
+                    help="time the extend (prefill) attention mla_extend_fp8 on a named workload")
     ap.add_argument("--write", action="store_true",
                     help="time the BF16 -> FP8 write path (scatter_cast_bf16_fp8) instead")
     return ap.parse_args()
@@ -149,6 +153,9 @@ def main():
         return
     if args.write:
         print(json.dumps(write_path(fm, workloads, torch, dev)), flush=True)
+        return
+    if args.extend:
+        print(json.dumps(extend_bench(fm, workloads, torch, dev, args)), flush=True)
         return
     if args.serving_step:
         print(json.dumps(serving_step(fm, workloads, torch, dev, args)), flush=True)
@@ -322,6 +329,85 @@ def cast_path_step(fm, workloads, torch, dev, args):
         "gather_then_attend_us_per_layer": round(gather_path_ms * 1e3 / L, 2),
         "fused_speedup_vs_cast_then_attend": round(cast_path_ms / fused_ms, 1),
         "fused_speedup_vs_gather_then_attend": round(gather_path_ms / fused_ms, 2),
+    }
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def extend_bench(fm, workloads, torch, dev, args):
+    """mla_extend_fp8 on a named extend workload: device time per call, MFMA
+    throughput against the BF16 dense peak (the work is 2 * H * 1088 flops per
+    (query token, visible cache token) pair) and cache bytes per second.
+    Beside it, the same attention as one decode request per query token
+    (mla_decode_fp8 over each token's visible prefix, index lists expanded on
+    the host): what sharing each KV tile among a block's tokens saves."""
+    import numpy as np
+    w = workloads.extend_config(args.extend, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = torch.empty((w.total_q, w.H, 512), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(256, fm.mla_extend_fp8_workspace_bytes(w.B, w.H, w.total_q)),
+                     dtype=torch.uint8, device=dev)
+
+    def ext():
+        fm.mla_extend_fp8(w.q, w.pool, w.qo_indptr, w.kv_indptr, w.kv_indices, w.scale,
+                          w.sm_scale, causal=w.causal, out=out, workspace=ws)
+
+    # per-token decode form: request r = query token, its visible prefix as the index list
+    qo = w.qo_indptr.cpu().numpy()
+    kv = w.kv_indptr.cpu().numpy()
+    idx = w.kv_indices.cpu().numpy()
+    lists, lens = [], []
+    for b in range(w.B):
+        ql, kl = int(qo[b + 1] - qo[b]), int(kv[b + 1] - kv[b])
+        for i in range(ql):
+            n = max(0, min(kl, kl - ql + i + 1)) if w.causal else kl
+            lists.append(idx[kv[b]:kv[b] + n])
+            lens.append(n)
+    tok_indptr = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    tok_indices = torch.from_numpy(np.concatenate(lists).astype(np.int32)).to(dev)
+    out_d = torch.empty_like(out)
+    ws_d = torch.empty(max(256, fm.mla_decode_fp8_workspace_bytes(w.total_q, w.H, int(sum(lens)))),
+                       dtype=torch.uint8, device=dev)
+
+    def per_token():
+        fm.mla_decode_fp8(w.q, w.pool, tok_indptr, tok_indices, w.scale, w.sm_scale, out=out_d,
+                          workspace=ws_d)
+
+    def timed(fn, k):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) * 1e3 / k
+
+    K = max(5, min(args.steps, 100))
+    us = timed(ext, K)
+    us_tok = timed(per_token, K)
+    pairs = w.visible_tokens()
+    flops = 2.0 * w.H * 1088 * pairs
+    tflops = flops / (us * 1e-6) / 1e12
+    return {
+        "metric": "extend attention over the FP8 cache: TFLOP/s (MFMA-bound) + us/call",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "higher_is_better": True,
+        "data": "synthetic", "dtype": "bf16 (fp8 KV)", "steps": K,
+        "config": {"workload": w.name, "total_q": w.total_q, "heads": w.H,
+                   "cache_tokens": int(w.kv_lens.sum()), "visible_pairs": pairs,
+                   "causal": w.causal},
+        "us_per_call": round(us, 2),
+        "query_tokens_per_s": round(w.total_q / (us * 1e-6), 1),
+        "cache_GBps": round(w.kv_bytes() / (us * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "one mla_extend_fp8 call: pre-pass + mla_split_h64_kernel<true> + combine"},
+        "per_token_decode_us": round(us_tok, 2),
+        "speedup_vs_per_token_decode": round(us_tok / us, 2),
     }
 
 
