@@ -37,7 +37,10 @@ if ROOT not in sys.path:
 METRIC = "useful KV GB/s (% of HBM peak) + µs/call, FP8 MLA decode, batch 40, 4k ctx"
 HBM_PEAK_GBPS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "mla_decode_batch40_counters.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "fp8_paged_mla_amd", "csrc", "mla_decode.hip")
+# the sources the batch-40 decode kernels are compiled from (the counter file
+# records their digest, so stale counters are never reported)
+KERNEL_SOURCES = [os.path.join(ROOT, "fp8_paged_mla_amd", "csrc", f)
+                  for f in ("mla_decode.hip", "decode_common.h", "device_common.h")]
 
 
 def parse_args():
@@ -62,9 +65,12 @@ def parse_args():
     return ap.parse_args()
 
 
-def source_digest(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(launch_units):
@@ -79,7 +85,7 @@ def read_traffic(launch_units):
             if line and not line.startswith("#") and "=" in line:
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("source_sha256_16") != source_digest(KERNEL_SOURCE):
+    if vals.get("source_sha256_16") != source_digest(KERNEL_SOURCES):
         return None
     try:
         return float(vals["hbm_bytes_per_call"])
