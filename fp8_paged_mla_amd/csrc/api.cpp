@@ -123,6 +123,7 @@ int mla_extend_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
       total_kv > kMaxTokens || num_slots < 0 || num_slots > kMaxSlots)
     return FP8MLA_ERR_BAD_SHAPE;
   if (total_kv > 0 && num_slots == 0) return FP8MLA_ERR_BAD_SHAPE;
+  if (total_q * num_heads > (int64_t)INT32_MAX) return FP8MLA_ERR_BAD_SHAPE;  // query rows
   if (!isfinite(scale) || !(scale > 0.0f) || !isfinite(sm_scale)) return FP8MLA_ERR_BAD_SCALAR;
   if (total_q == 0) return FP8MLA_OK;
   if (!q || !qo_indptr || !kv_indptr || !out || !workspace) return FP8MLA_ERR_NULL_PTR;

@@ -227,6 +227,7 @@ size_t mla_decode_bf16_workspace_bytes(int32_t batch, int32_t num_heads, int64_t
  *               total_q) bytes of scratch (no initialisation needed,
  *               garbage afterwards; NULL allowed when total_q == 0)
  *   1 <= batch, 1 <= num_heads <= FP8MLA_MAX_HEADS, 0 <= total_q < 2^29,
+ *   total_q * num_heads <= 2^31 - 1,
  *   0 <= total_kv <= 2^31 - 1; num_slots >= 1 when total_kv > 0;
  *   scale finite > 0, sm_scale finite.
  * The index arrays are read on the device only.  Out-of-range indptr

@@ -218,6 +218,7 @@ def test_mla_extend_validation():
     assert ext(tq=-1) == ERR_SHAPE
     assert ext(tq=1 << 29) == ERR_SHAPE
     assert ext(tkv=-1) == ERR_SHAPE
+    assert ext(tq=(1 << 29) - 1, H=256) == ERR_SHAPE   # query rows past 2^31 - 1
     assert ext(tkv=1 << 31) == ERR_SHAPE
     assert ext(slots=0) == ERR_SHAPE
     assert ext(scale=0.0) == ERR_SCALAR
