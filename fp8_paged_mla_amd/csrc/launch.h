@@ -32,14 +32,13 @@ enum class DecodeKernel { kFp8, kFp8H64, kBf16 };
 // parallelism.
 constexpr int kH64MinHeads = 64;
 // The 64-row kernel computes scores on the FP8 MFMA (16x16x128 f8f6f4) from a
-// two-part FP8 query made by a pre-pass (mla_decode_h64.hip).
-constexpr bool kH64QueryFp8 = true;
-// Workspace of that pre-pass for `rows` query rows: hi and lo codes (576
-// bytes each per row) and 1 / s (4 bytes per row), 256-byte aligned parts.
+// two-part FP8 query made by a pre-pass (mla_decode_h64.hip).  Workspace of
+// that pre-pass for `rows` query rows: hi and lo codes (576 bytes each per
+// row) and 1 / s (4 bytes per row), 256-byte aligned parts.
 inline size_t q8_workspace_bytes(int64_t rows) {
   const size_t codes = ((size_t)rows * 576 + 255) / 256 * 256;
   const size_t inv = ((size_t)rows * 4 + 255) / 256 * 256;
-  return kH64QueryFp8 ? 2 * codes + inv : 0;
+  return 2 * codes + inv;
 }
 struct Q8Buffers {
   uint8_t* hi;

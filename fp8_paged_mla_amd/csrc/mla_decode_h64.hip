@@ -8,32 +8,33 @@
 // slice of the math.  Here one workgroup (8 waves) takes 64 heads (four
 // groups of 16) over 64-token tiles, so a tile is copied and exchanged once
 // per 64 heads and each wave issues four times the MFMA work per tile:
-//  * wave w owns head group w & 3 (its 16 heads' query in registers) and
-//    tokens [32(w >> 2), +32) of the tile for the score product
-//    S^T = K q^T (MFMA 16x16x32 bf16, two 16-token blocks);
+//  * wave w owns head group w & 3 and tokens [32(w >> 2), +32) of the tile
+//    for the score product S^T = K q^T, two 16-token blocks on the FP8 MFMA
+//    16x16x128 (below);
 //  * the two waves of a head group exchange maxima and probabilities
 //    through LDS;
 //  * for P.V, wave w owns output columns [256(w >> 2), +256) of its head
-//    group: O^T = V^T P^T over all 64 tokens (16 column blocks of 16), with
-//    the transposed FP8 value operand read by ds_read_b64_tr_b8.
+//    group: O^T = V^T P^T over all 64 tokens (16 column blocks of 16, MFMA
+//    16x16x32 bf16), with the transposed FP8 value operand read by
+//    ds_read_b64_tr_b8.
 // Rows are copied global -> LDS (global_load_lds) into three slots of 64
 // rows: tile k+2 goes into the slot of tile k-1 once every wave has finished
 // tile k-1's value reads (the first barrier of tile k), ~1.5 tiles ahead.
 //
-// FP8-query mode (Q8): the score product S^T = K q^T runs on the FP8 MFMA
-// 16x16x128 (f8f6f4, E4M3 operands), which is 3.5x the BF16 MFMA's rate on
-// this part, and no K byte is converted (the BF16 product converts every K
-// byte once per head group: half the kernel's VALU work).  A single E4M3
-// query would miss the attention tolerance, so q_split_kernel first writes
-// per query row the codes of q * s (hi) and of the 16x rounding residual
-// (lo), s a power of two putting the row's largest magnitude in [224, 448]:
-// hi + lo / 16 keeps about 8 significant bits, as BF16 does.  A workgroup
-// keeps its rows' hi codes in registers (40 VGPRs per lane) and copies their
-// lo rows into a fourth LDS slot like KV rows; scores are (K.hi + K.lo / 16)
-// / s.  Lane (t, g) of the MFMA holds bytes 32g .. 32g+31 of each 128-dim
-// chunk for both operands (the instruction sums over any common pairing);
-// 576 dims are four full chunks and a fifth whose lanes g = 2, 3 repeat dims
-// 512..575 against zero hi and lo codes.
+// Scores on the FP8 MFMA: v_mfma_f32_16x16x128_f8f6f4 runs at 3.5x the BF16
+// MFMA's rate on this part and takes K straight from the FP8 tile: no K
+// byte is converted (converting K once per head group was a quarter of the
+// kernel's VALU work, which bounds it).  A single E4M3 query would miss the
+// attention tolerance, so q_split_kernel first writes per query row the
+// codes of q * s (hi) and of the 16x rounding residual (lo), s a power of
+// two putting the row's largest magnitude in [224, 448]: hi + lo / 16 keeps
+// about 8 significant bits, as BF16 does.  A workgroup keeps its rows' hi
+// codes in registers (40 VGPRs per lane) and copies their lo rows into a
+// fourth LDS slot like KV rows; scores are (K.hi + K.lo / 16) / s.  Lane
+// (t, g) of the MFMA holds bytes 32g .. 32g+31 of each 128-dim chunk for both
+// operands (the instruction sums over any common pairing); 576 dims are four
+// full chunks and a fifth whose lanes g = 2, 3 repeat dims 512..575 against
+// zero hi and lo codes.
 //
 // The extend instantiation (EXT) serves several query tokens per request:
 // the 64 rows of a workgroup are (token, head) pairs of one virtual request
@@ -58,49 +59,11 @@ constexpr int NSLOTS = 3;
 constexpr int ROW_SLOTS = KV_CHUNKS + 1;          // 37 (odd 16-byte stride)
 constexpr int ROWB = 16 * ROW_SLOTS;              // 592
 constexpr int TILE_BYTES = TILE * ROWB;           // 37888
-constexpr int KSTEPS = KV_WIDTH / 64;             // 9
-constexpr int QSTEPS = 2 * KSTEPS;                // 18
 constexpr int ROWS_PER_WAVE = TILE / NWAVES;      // 8 rows copied by each wave
 constexpr int DMA_OPS = (ROWS_PER_WAVE * ROW_SLOTS + 63) / 64;  // 5
 constexpr int VBLOCKS = (V_WIDTH / 2) / 16;       // 16 output blocks per wave
 static_assert(TILE == 1 << TILE_SHIFT, "tile size");
 static_assert(TILE == kH64TileTokens, "host and kernel tile sizes agree");
-
-__device__ __forceinline__ void issue_load_q(bf16x8_t (&q)[QSTEPS], const uint16_t* qp) {
-  // 9 pairs of 16-byte pieces 64 elements (128 bytes) apart
-  asm volatile(
-      "global_load_dwordx4 %0, %18, off\n\t"
-      "global_load_dwordx4 %1, %18, off offset:16\n\t"
-      "global_load_dwordx4 %2, %18, off offset:128\n\t"
-      "global_load_dwordx4 %3, %18, off offset:144\n\t"
-      "global_load_dwordx4 %4, %18, off offset:256\n\t"
-      "global_load_dwordx4 %5, %18, off offset:272\n\t"
-      "global_load_dwordx4 %6, %18, off offset:384\n\t"
-      "global_load_dwordx4 %7, %18, off offset:400\n\t"
-      "global_load_dwordx4 %8, %18, off offset:512\n\t"
-      "global_load_dwordx4 %9, %18, off offset:528\n\t"
-      "global_load_dwordx4 %10, %18, off offset:640\n\t"
-      "global_load_dwordx4 %11, %18, off offset:656\n\t"
-      "global_load_dwordx4 %12, %18, off offset:768\n\t"
-      "global_load_dwordx4 %13, %18, off offset:784\n\t"
-      "global_load_dwordx4 %14, %18, off offset:896\n\t"
-      "global_load_dwordx4 %15, %18, off offset:912\n\t"
-      "global_load_dwordx4 %16, %18, off offset:1024\n\t"
-      "global_load_dwordx4 %17, %18, off offset:1040"
-      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]),
-        "=&v"(q[7]), "=&v"(q[8]), "=&v"(q[9]), "=&v"(q[10]), "=&v"(q[11]), "=&v"(q[12]),
-        "=&v"(q[13]), "=&v"(q[14]), "=&v"(q[15]), "=&v"(q[16]), "=&v"(q[17])
-      : "v"(qp));
-}
-
-__device__ __forceinline__ void pin_q(bf16x8_t (&q)[QSTEPS]) {
-  asm volatile(""
-               : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]),
-                 "+v"(q[6]), "+v"(q[7]), "+v"(q[8]));
-  asm volatile(""
-               : "+v"(q[9]), "+v"(q[10]), "+v"(q[11]), "+v"(q[12]), "+v"(q[13]), "+v"(q[14]),
-                 "+v"(q[15]), "+v"(q[16]), "+v"(q[17]));
-}
 
 // Wait until at most n vector-memory operations are outstanding (n is
 // wave-uniform and one of the counts this pipeline produces; any other value
@@ -111,8 +74,6 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
     case 5: wait_vm<5>(); break;
     case 6: wait_vm<6>(); break;
     case 11: wait_vm<11>(); break;
-    case 19: wait_vm<19>(); break;
-    case 24: wait_vm<24>(); break;
     default: wait_vm<0>(); break;
   }
 }
@@ -191,11 +152,11 @@ __global__ __launch_bounds__(64 * QSPLIT_ROWS) void q_split_kernel(
 // LDS banks.
 __device__ __forceinline__ int tile_row(int B, int m) { return 16 * B + ((B & 1) ? (m ^ 12) : m); }
 
-template <bool EXT, bool Q8>
+template <bool EXT>
 __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSLOTS * TILE_BYTES];
-  // Q8: the workgroup's 64 lo rows (row r at r * ROWB), then 32 zero bytes
-  __shared__ __attribute__((aligned(16))) uint8_t qlo_lds[Q8 ? TILE_BYTES + 32 : 16];
+  // the workgroup's 64 lo query rows (row r at r * ROWB), then 32 zero bytes
+  __shared__ __attribute__((aligned(16))) uint8_t qlo_lds[TILE_BYTES + 32];
   __shared__ float mx_lds[NWAVES][HEADS];
   __shared__ uint2 p_lds[NWAVES][2][64];
   __shared__ float l_lds[NWAVES][HEADS];
@@ -290,52 +251,33 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     }
     return qrow * p.H + min(h, p.H - 1);
   };
-  auto q_lane_ptr = [&](const Cursor& c) -> const uint16_t* {
-    int64_t qrow = c.b;
-    if constexpr (EXT) qrow = c.q_row0() + min(tk, c.q_tokens() - 1);
-    return p.q + (qrow * p.H + min(head, p.H - 1)) * KV_WIDTH + 16 * g;
-  };
   // rows without a query (heads past H; extend: tokens past the block) keep a zero query
   auto row_idle = [&]() -> bool {
     if constexpr (EXT) return head >= p.H || tk >= cc.q_tokens();
     return head >= p.H;
   };
-  bf16x8_t qr[Q8 ? 1 : QSTEPS];        // BF16 scores: the query
-  i32x8_t qh[Q8 ? Q8_CHUNKS : 1];      // Q8: hi codes per 128-dim chunk
-  float q_inv = 1.f;                   // Q8: 1 / s of this lane's row
+  i32x8_t qh[Q8_CHUNKS];  // hi codes of this lane's query row, per 128-dim chunk
+  float q_inv = 1.f;      // 1 / s of this lane's row
   const uint32_t qlo_base = (uint32_t)(uintptr_t)(
       (__attribute__((address_space(3))) uint8_t*)&qlo_lds[0]);
-  constexpr int Q_LOADS = Q8 ? DMA_OPS : QSTEPS;  // memory ops of a query load
-  // issue the query loads of request c (Q8: the lo rows into LDS)
+  // issue the lo query rows of request c into LDS (DMA_OPS memory ops)
   auto issue_q = [&](const Cursor& c) {
-    if constexpr (Q8) {
-      const int64_t ri = row_index(c, ROWS_PER_WAVE * w + (t & 7));
-      issue_rows(p.q_lo, 0xFFFFFFFFu, qlo_base, (int32_t)ri);
-    } else {
-      issue_load_q(qr, q_lane_ptr(c));
-    }
+    const int64_t ri = row_index(c, ROWS_PER_WAVE * w + (t & 7));
+    issue_rows(p.q_lo, 0xFFFFFFFFu, qlo_base, (int32_t)ri);
   };
-  // the query loads have landed (Q8: for this wave; the caller synchronises
-  // the workgroup before the lo rows are read)
+  // this wave's lo rows have landed (the caller synchronises the workgroup
+  // before they are read): load the hi codes and 1 / s of this lane's row
   auto finish_q = [&]() {
-    if constexpr (Q8) {
-      const int64_t ri = row_index(cc, hgl * HEADS + t);
-      const uint8_t* hp = p.q_hi + ri * KV_WIDTH;
-      const bool idle = row_idle();
+    const int64_t ri = row_index(cc, hgl * HEADS + t);
+    const uint8_t* hp = p.q_hi + ri * KV_WIDTH;
+    const bool idle = row_idle();
 #pragma unroll
-      for (int c = 0; c < Q8_CHUNKS; ++c) {
-        const int off = c < Q8_CHUNKS - 1 ? 128 * c + 32 * g : 512 + 32 * (g & 1);
-        const i32x8_t v = *reinterpret_cast<const i32x8_t*>(hp + off);
-        qh[c] = idle || (c == Q8_CHUNKS - 1 && g >= 2) ? i32x8_t{} : v;
-      }
-      q_inv = p.q_inv[ri];
-    } else {
-      pin_q(qr);
-      if (row_idle()) {
-#pragma unroll
-        for (int s = 0; s < QSTEPS; ++s) qr[s] = bf16x8_t{};
-      }
+    for (int c = 0; c < Q8_CHUNKS; ++c) {
+      const int off = c < Q8_CHUNKS - 1 ? 128 * c + 32 * g : 512 + 32 * (g & 1);
+      const i32x8_t v = *reinterpret_cast<const i32x8_t*>(hp + off);
+      qh[c] = idle || (c == Q8_CHUNKS - 1 && g >= 2) ? i32x8_t{} : v;
     }
+    q_inv = p.q_inv[ri];
   };
 
   // Prologue: indices of tiles 0 and 1; query, rows of tile 0, index of tile
@@ -345,9 +287,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   wait_vm<0>();
   pin(ixA);
   pin(ixB);
-  if constexpr (Q8) {  // 32 zero bytes after the lo rows (the fifth chunk's lanes g = 2, 3)
-    if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(qlo_lds + TILE_BYTES)[threadIdx.x] = 0u;
-  }
+  // 32 zero bytes after the lo rows (the fifth chunk's lanes g = 2, 3)
+  if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(qlo_lds + TILE_BYTES)[threadIdx.x] = 0u;
   issue_q(cc);
   issue_tile(0, ixA);
   ixA = load_next_index();
@@ -361,9 +302,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   // wave's column base 256 half.
   const int k_row0 = tile_row(2 * half, t) * ROWB;
   const int k_row1 = tile_row(2 * half + 1, t) * ROWB;
-  const int k_off0 = k_row0 + 16 * g;
-  const int k_off1 = k_row1 + 16 * g;
-  const int qlo_row = (hgl * HEADS + t) * ROWB;  // Q8: this lane's row of the lo block
+  const int qlo_row = (hgl * HEADS + t) * ROWB;  // this lane's row of the lo block
   const int tr_row0 = (t >> 1) < 4 ? 4 * g + (t >> 1) : 16 + 4 * (g ^ 3) + (t >> 1) - 4;
   const int tr_off = tr_row0 * ROWB + 8 * (t & 1) + 256 * half;
   const int s_tok0 = 32 * half + 4 * g;             // block 2 half (even)
@@ -440,43 +379,27 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     if (q_pending) {  // issued before the rows of tile k+1: those may stay in flight
       wait_vm_upto(k + 1 < ntiles ? DMA_OPS : 0);
       finish_q();
-      if constexpr (Q8) __syncthreads();  // every wave's lo rows landed
+      __syncthreads();  // every wave's lo rows landed
       q_pending = false;
     }
 
+    // a0 / c0 from the hi codes, a1 / c1 from the lo codes (weight 1/16)
     f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, c0 = a0, c1 = a0;
-    float sc0 = p.score_scale, sc1 = p.score_scale;  // score = a0 * sc0 + a1 * sc1
-    if constexpr (Q8) {
-      // a0 / c0 from the hi codes, a1 / c1 from the lo codes (weight 1/16)
-      const uint8_t* kp0 = slot + k_row0;
-      const uint8_t* kp1 = slot + k_row1;
+    const uint8_t* kp0 = slot + k_row0;
+    const uint8_t* kp1 = slot + k_row1;
 #pragma unroll
-      for (int c = 0; c < Q8_CHUNKS; ++c) {
-        const int ko = c < Q8_CHUNKS - 1 ? 128 * c + 32 * g : 512 + 32 * (g & 1);
-        const i32x8_t k0 = *reinterpret_cast<const i32x8_a16_t*>(kp0 + ko);
-        const i32x8_t k1 = *reinterpret_cast<const i32x8_a16_t*>(kp1 + ko);
-        const i32x8_t ql = *reinterpret_cast<const i32x8_a16_t*>(
-            qlo_lds + (c < Q8_CHUNKS - 1 || g < 2 ? qlo_row + ko : TILE_BYTES));
-        a0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k0, qh[c], a0, 0, 0, 0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k0, ql, a1, 0, 0, 0, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k1, qh[c], c0, 0, 0, 0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k1, ql, c1, 0, 0, 0, 0, 0, 0);
-      }
-      sc0 = p.score_scale * q_inv;
-      sc1 = sc0 * 0.0625f;
-    } else {
-      const uint8_t* kp0 = slot + k_off0;
-      const uint8_t* kp1 = slot + k_off1;
-#pragma unroll
-      for (int i = 0; i < KSTEPS; ++i) {
-        const u32x4_t kv0 = *reinterpret_cast<const u32x4_t*>(kp0 + 64 * i);
-        const u32x4_t kv1 = *reinterpret_cast<const u32x4_t*>(kp1 + 64 * i);
-        a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[0], kv0[1]), qr[2 * i], a0, 0, 0, 0);
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[0], kv1[1]), qr[2 * i], c0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[2], kv0[3]), qr[2 * i + 1], a1, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[2], kv1[3]), qr[2 * i + 1], c1, 0, 0, 0);
-      }
+    for (int c = 0; c < Q8_CHUNKS; ++c) {
+      const int ko = c < Q8_CHUNKS - 1 ? 128 * c + 32 * g : 512 + 32 * (g & 1);
+      const i32x8_t k0 = *reinterpret_cast<const i32x8_a16_t*>(kp0 + ko);
+      const i32x8_t k1 = *reinterpret_cast<const i32x8_a16_t*>(kp1 + ko);
+      const i32x8_t ql = *reinterpret_cast<const i32x8_a16_t*>(
+          qlo_lds + (c < Q8_CHUNKS - 1 || g < 2 ? qlo_row + ko : TILE_BYTES));
+      a0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k0, qh[c], a0, 0, 0, 0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k0, ql, a1, 0, 0, 0, 0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k1, qh[c], c0, 0, 0, 0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k1, ql, c1, 0, 0, 0, 0, 0, 0);
     }
+    const float sc0 = p.score_scale * q_inv, sc1 = sc0 * 0.0625f;
     float s0[4], s1[4];
     float lmax = -INFINITY;
 #pragma unroll
@@ -526,7 +449,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     p_lds[w][0][lane] = make_uint2(p01, p23);
     p_lds[w][1][lane] = make_uint2(q01, q23);
     // rows of tile k+1 landed (younger: index k+3, maybe a query, rows k+2)
-    if (k + 1 < ntiles) wait_vm_upto(1 + (new_q ? Q_LOADS : 0) + (k + 2 < ntiles ? DMA_OPS : 0));
+    if (k + 1 < ntiles) wait_vm_upto(1 + (new_q ? DMA_OPS : 0) + (k + 2 < ntiles ? DMA_OPS : 0));
     __syncthreads();
 
     // P.V over the tile's 64 tokens: step st covers blocks 2st and 2st+1,
@@ -578,25 +501,17 @@ hipError_t launch_mla_decode_h64(const uint16_t* q, const uint8_t* kv_pool, int6
   decode::SplitParams sp = make_split_params(q, kv_pool, num_slots, kv_indptr, kv_indices,
                                              total_tokens, batch, num_heads, scale, sm_scale, out,
                                              workspace, pl);
-  hipError_t e;
-  if (kH64QueryFp8) {
-    e = launch_q_split(q, (int64_t)batch * num_heads, reinterpret_cast<char*>(workspace) + pl.q8_offset,
-                       sp, stream);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mla_split_h64_kernel<false, true>), dim3(pl.grid), dim3(THREADS), 0, stream, sp);
-  } else {
-    hipLaunchKernelGGL((mla_split_h64_kernel<false, false>), dim3(pl.grid), dim3(THREADS), 0, stream, sp);
-  }
+  hipError_t e = launch_q_split(q, (int64_t)batch * num_heads,
+                                reinterpret_cast<char*>(workspace) + pl.q8_offset, sp, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_split_h64_kernel<false>, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
   e = hipGetLastError();
   if (e != hipSuccess || total_tokens == 0) return e;
   return launch_mla_combine(sp, stream);
 }
 
 hipError_t launch_mla_split_h64_extend(const decode::SplitParams& sp, int grid, hipStream_t stream) {
-  if (kH64QueryFp8)
-    hipLaunchKernelGGL((mla_split_h64_kernel<true, true>), dim3(grid), dim3(THREADS), 0, stream, sp);
-  else
-    hipLaunchKernelGGL((mla_split_h64_kernel<true, false>), dim3(grid), dim3(THREADS), 0, stream, sp);
+  hipLaunchKernelGGL(mla_split_h64_kernel<true>, dim3(grid), dim3(THREADS), 0, stream, sp);
   return hipGetLastError();
 }
 
