@@ -43,12 +43,6 @@ struct SplitParams {
   const int2* vinfo;
   int32_t rows_per_tok;  // query rows per token (heads rounded up to 16) if <= 64, else 0
   int32_t causal;
-  // FP8-query scores (64-row kernel): per query row (row index = query
-  // token * H + head), E4M3 codes of q * s (q_hi) and of the 16x residual
-  // (q_lo), 576 bytes each, and 1 / s (q_inv), written by the split pre-pass.
-  const uint8_t* q_hi;
-  const uint8_t* q_lo;
-  const float* q_inv;
 };
 
 constexpr int kExtQ0Bits = 29;                 // first query row in the low 29 bits of vinfo.y

@@ -19,9 +19,4 @@ hipError_t launch_mla_combine(const decode::SplitParams& sp, hipStream_t stream)
 // The 64-row split kernel in its extend form (virtual requests, causal limits).
 hipError_t launch_mla_split_h64_extend(const decode::SplitParams& sp, int grid, hipStream_t stream);
 
-// FP8-query pre-pass for `rows` query rows of q: writes the hi / lo codes and
-// 1 / s into `buffers` (q8_workspace_bytes(rows) bytes) and points sp at them.
-hipError_t launch_q_split(const uint16_t* q, int64_t rows, void* buffers, decode::SplitParams& sp,
-                          hipStream_t stream);
-
 }  // namespace fp8mla

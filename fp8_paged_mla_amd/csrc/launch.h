@@ -31,25 +31,6 @@ enum class DecodeKernel { kFp8, kFp8H64, kBf16 };
 // kernel, which has four times as many workgroups per segment, exposes more
 // parallelism.
 constexpr int kH64MinHeads = 64;
-// The 64-row kernel computes scores on the FP8 MFMA (16x16x128 f8f6f4) from a
-// two-part FP8 query made by a pre-pass (mla_decode_h64.hip).  Workspace of
-// that pre-pass for `rows` query rows: hi and lo codes (576 bytes each per
-// row) and 1 / s (4 bytes per row), 256-byte aligned parts.
-inline size_t q8_workspace_bytes(int64_t rows) {
-  const size_t codes = ((size_t)rows * 576 + 255) / 256 * 256;
-  const size_t inv = ((size_t)rows * 4 + 255) / 256 * 256;
-  return 2 * codes + inv;
-}
-struct Q8Buffers {
-  uint8_t* hi;
-  uint8_t* lo;
-  float* inv;
-};
-inline Q8Buffers q8_buffers(void* base, int64_t rows) {
-  const size_t codes = ((size_t)rows * 576 + 255) / 256 * 256;
-  uint8_t* b = reinterpret_cast<uint8_t*>(base);
-  return Q8Buffers{b, b + codes, reinterpret_cast<float*>(b + 2 * codes)};
-}
 constexpr int kH64MinTilesPerCu = 4;
 
 struct DecodePlan {
@@ -62,7 +43,6 @@ struct DecodePlan {
   int32_t grid;        // launched workgroups (>= items)
   size_t part_o_offset;  // byte offset of the partial outputs inside the workspace
   size_t lse_offset;   // byte offset of the lse array inside the workspace
-  size_t q8_offset;    // kFp8H64: byte offset of the FP8-query buffers (q8_buffers)
   size_t workspace_bytes;
 };
 
@@ -118,7 +98,6 @@ struct ExtendPlan {
   size_t pieces_offset;   // int2 [vmax]: (segment of the first piece, pieces)
   size_t part_o_offset;   // fp16 [(nseg + vmax) * Hp * 512]
   size_t lse_offset;      // float [(nseg + vmax) * Hp]
-  size_t q8_offset;       // FP8-query buffers for total_q * heads rows (q8_buffers)
   size_t workspace_bytes; // also holds the header {virtual requests, CSR total} at offset 0
 };
 

@@ -460,10 +460,7 @@ DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_token
   const size_t lse_bytes = npieces * pl.Hp * sizeof(float);
   pl.part_o_offset = (ranges_bytes + 255) / 256 * 256;
   pl.lse_offset = pl.part_o_offset + (o_bytes + 255) / 256 * 256;
-  pl.q8_offset = pl.lse_offset + (lse_bytes + 255) / 256 * 256;
-  pl.workspace_bytes = pl.q8_offset;
-  if (kernel == DecodeKernel::kFp8H64)
-    pl.workspace_bytes += q8_workspace_bytes((int64_t)batch * num_heads);
+  pl.workspace_bytes = pl.lse_offset + (lse_bytes + 255) / 256 * 256;
   return pl;
 }
 

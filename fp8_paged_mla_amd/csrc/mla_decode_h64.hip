@@ -8,33 +8,17 @@
 // slice of the math.  Here one workgroup (8 waves) takes 64 heads (four
 // groups of 16) over 64-token tiles, so a tile is copied and exchanged once
 // per 64 heads and each wave issues four times the MFMA work per tile:
-//  * wave w owns head group w & 3 and tokens [32(w >> 2), +32) of the tile
-//    for the score product S^T = K q^T, two 16-token blocks on the FP8 MFMA
-//    16x16x128 (below);
+//  * wave w owns head group w & 3 (its 16 heads' query in registers) and
+//    tokens [32(w >> 2), +32) of the tile for the score product
+//    S^T = K q^T (MFMA 16x16x32 bf16, two 16-token blocks);
 //  * the two waves of a head group exchange maxima and probabilities
 //    through LDS;
 //  * for P.V, wave w owns output columns [256(w >> 2), +256) of its head
-//    group: O^T = V^T P^T over all 64 tokens (16 column blocks of 16, MFMA
-//    16x16x32 bf16), with the transposed FP8 value operand read by
-//    ds_read_b64_tr_b8.
+//    group: O^T = V^T P^T over all 64 tokens (16 column blocks of 16), with
+//    the transposed FP8 value operand read by ds_read_b64_tr_b8.
 // Rows are copied global -> LDS (global_load_lds) into three slots of 64
 // rows: tile k+2 goes into the slot of tile k-1 once every wave has finished
 // tile k-1's value reads (the first barrier of tile k), ~1.5 tiles ahead.
-//
-// Scores on the FP8 MFMA: v_mfma_f32_16x16x128_f8f6f4 runs at 3.5x the BF16
-// MFMA's rate on this part and takes K straight from the FP8 tile: no K
-// byte is converted (converting K once per head group was a quarter of the
-// kernel's VALU work, which bounds it).  A single E4M3 query would miss the
-// attention tolerance, so q_split_kernel first writes per query row the
-// codes of q * s (hi) and of the 16x rounding residual (lo), s a power of
-// two putting the row's largest magnitude in [224, 448]: hi + lo / 16 keeps
-// about 8 significant bits, as BF16 does.  A workgroup keeps its rows' hi
-// codes in registers (40 VGPRs per lane) and copies their lo rows into a
-// fourth LDS slot like KV rows; scores are (K.hi + K.lo / 16) / s.  Lane
-// (t, g) of the MFMA holds bytes 32g .. 32g+31 of each 128-dim chunk for both
-// operands (the instruction sums over any common pairing); 576 dims are four
-// full chunks and a fifth whose lanes g = 2, 3 repeat dims 512..575 against
-// zero hi and lo codes.
 //
 // The extend instantiation (EXT) serves several query tokens per request:
 // the 64 rows of a workgroup are (token, head) pairs of one virtual request
@@ -59,11 +43,49 @@ constexpr int NSLOTS = 3;
 constexpr int ROW_SLOTS = KV_CHUNKS + 1;          // 37 (odd 16-byte stride)
 constexpr int ROWB = 16 * ROW_SLOTS;              // 592
 constexpr int TILE_BYTES = TILE * ROWB;           // 37888
+constexpr int KSTEPS = KV_WIDTH / 64;             // 9
+constexpr int QSTEPS = 2 * KSTEPS;                // 18
 constexpr int ROWS_PER_WAVE = TILE / NWAVES;      // 8 rows copied by each wave
 constexpr int DMA_OPS = (ROWS_PER_WAVE * ROW_SLOTS + 63) / 64;  // 5
 constexpr int VBLOCKS = (V_WIDTH / 2) / 16;       // 16 output blocks per wave
 static_assert(TILE == 1 << TILE_SHIFT, "tile size");
 static_assert(TILE == kH64TileTokens, "host and kernel tile sizes agree");
+
+__device__ __forceinline__ void issue_load_q(bf16x8_t (&q)[QSTEPS], const uint16_t* qp) {
+  // 9 pairs of 16-byte pieces 64 elements (128 bytes) apart
+  asm volatile(
+      "global_load_dwordx4 %0, %18, off\n\t"
+      "global_load_dwordx4 %1, %18, off offset:16\n\t"
+      "global_load_dwordx4 %2, %18, off offset:128\n\t"
+      "global_load_dwordx4 %3, %18, off offset:144\n\t"
+      "global_load_dwordx4 %4, %18, off offset:256\n\t"
+      "global_load_dwordx4 %5, %18, off offset:272\n\t"
+      "global_load_dwordx4 %6, %18, off offset:384\n\t"
+      "global_load_dwordx4 %7, %18, off offset:400\n\t"
+      "global_load_dwordx4 %8, %18, off offset:512\n\t"
+      "global_load_dwordx4 %9, %18, off offset:528\n\t"
+      "global_load_dwordx4 %10, %18, off offset:640\n\t"
+      "global_load_dwordx4 %11, %18, off offset:656\n\t"
+      "global_load_dwordx4 %12, %18, off offset:768\n\t"
+      "global_load_dwordx4 %13, %18, off offset:784\n\t"
+      "global_load_dwordx4 %14, %18, off offset:896\n\t"
+      "global_load_dwordx4 %15, %18, off offset:912\n\t"
+      "global_load_dwordx4 %16, %18, off offset:1024\n\t"
+      "global_load_dwordx4 %17, %18, off offset:1040"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(q[4]), "=&v"(q[5]), "=&v"(q[6]),
+        "=&v"(q[7]), "=&v"(q[8]), "=&v"(q[9]), "=&v"(q[10]), "=&v"(q[11]), "=&v"(q[12]),
+        "=&v"(q[13]), "=&v"(q[14]), "=&v"(q[15]), "=&v"(q[16]), "=&v"(q[17])
+      : "v"(qp));
+}
+
+__device__ __forceinline__ void pin_q(bf16x8_t (&q)[QSTEPS]) {
+  asm volatile(""
+               : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]), "+v"(q[4]), "+v"(q[5]),
+                 "+v"(q[6]), "+v"(q[7]), "+v"(q[8]));
+  asm volatile(""
+               : "+v"(q[9]), "+v"(q[10]), "+v"(q[11]), "+v"(q[12]), "+v"(q[13]), "+v"(q[14]),
+                 "+v"(q[15]), "+v"(q[16]), "+v"(q[17]));
+}
 
 // Wait until at most n vector-memory operations are outstanding (n is
 // wave-uniform and one of the counts this pipeline produces; any other value
@@ -73,78 +95,10 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
     case 1: wait_vm<1>(); break;
     case 5: wait_vm<5>(); break;
     case 6: wait_vm<6>(); break;
-    case 11: wait_vm<11>(); break;
+    case 19: wait_vm<19>(); break;
+    case 24: wait_vm<24>(); break;
     default: wait_vm<0>(); break;
   }
-}
-
-constexpr int Q8_CHUNKS = 5;
-typedef __attribute__((ext_vector_type(8))) int i32x8_t;
-typedef i32x8_t __attribute__((aligned(16))) i32x8_a16_t;  // LDS rows are 16-byte aligned
-
-__device__ __forceinline__ float wave_max64(float x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-// Codes of 4 values (|x| <= 448), byte j = element j, and of their 16x residuals.
-__device__ __forceinline__ void e4m3_hi_lo(float x0, float x1, float x2, float x3, uint32_t& h,
-                                           uint32_t& l) {
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-  h = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, r, true);
-  const auto b01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, false);
-  const auto b23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, true);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32((x0 - b01[0]) * 16.f, (x1 - b01[1]) * 16.f, 0, false);
-  l = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32((x2 - b23[0]) * 16.f, (x3 - b23[1]) * 16.f, r, true);
-}
-
-// Eight BF16 values (16 bytes) times s -> 8 hi codes and 8 lo codes.
-__device__ __forceinline__ void split8(const u32x4_t v, float s, u32x2_t& hi, u32x2_t& lo) {
-  uint32_t h0, l0, h1, l1;
-  e4m3_hi_lo(bf16_bits_to_f32(v[0] & 0xFFFFu) * s, bf16_bits_to_f32(v[0] >> 16) * s,
-             bf16_bits_to_f32(v[1] & 0xFFFFu) * s, bf16_bits_to_f32(v[1] >> 16) * s, h0, l0);
-  e4m3_hi_lo(bf16_bits_to_f32(v[2] & 0xFFFFu) * s, bf16_bits_to_f32(v[2] >> 16) * s,
-             bf16_bits_to_f32(v[3] & 0xFFFFu) * s, bf16_bits_to_f32(v[3] >> 16) * s, h1, l1);
-  hi = u32x2_t{h0, h1};
-  lo = u32x2_t{l0, l1};
-}
-
-__device__ __forceinline__ float absmax8(const u32x4_t v) {
-  float m = 0.f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    m = fmaxf(m, fmaxf(fabsf(bf16_bits_to_f32(v[e] & 0xFFFFu)), fabsf(bf16_bits_to_f32(v[e] >> 16))));
-  return m;
-}
-
-// One wave per query row (576 BF16): lane l takes dims 8l..8l+7, lanes 0..7
-// also dims 512+8l..; writes hi and lo codes (576 bytes each) and 1 / s.
-constexpr int QSPLIT_ROWS = 4;
-__global__ __launch_bounds__(64 * QSPLIT_ROWS) void q_split_kernel(
-    const uint16_t* __restrict__ q, int64_t rows, uint8_t* __restrict__ hi,
-    uint8_t* __restrict__ lo, float* __restrict__ inv) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * QSPLIT_ROWS + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const uint16_t* src = q + row * KV_WIDTH;
-  const u32x4_t a = *reinterpret_cast<const u32x4_t*>(src + 8 * lane);
-  u32x4_t b = {0u, 0u, 0u, 0u};
-  if (lane < 8) b = *reinterpret_cast<const u32x4_t*>(src + 512 + 8 * lane);
-  const float amax = wave_max64(fmaxf(absmax8(a), absmax8(b)));
-  float s = 1.f;
-  if (amax > 0.f && amax <= 3.0e38f)  // 2^(e-1) <= 448 / amax
-    s = __builtin_amdgcn_ldexpf(1.f, __builtin_amdgcn_frexp_expf(448.f / amax) - 1);
-  u32x2_t h, l;
-  split8(a, s, h, l);
-  *reinterpret_cast<u32x2_t*>(hi + row * KV_WIDTH + 8 * lane) = h;
-  *reinterpret_cast<u32x2_t*>(lo + row * KV_WIDTH + 8 * lane) = l;
-  if (lane < 8) {
-    split8(b, s, h, l);
-    *reinterpret_cast<u32x2_t*>(hi + row * KV_WIDTH + 512 + 8 * lane) = h;
-    *reinterpret_cast<u32x2_t*>(lo + row * KV_WIDTH + 512 + 8 * lane) = l;
-  }
-  if (lane == 0) inv[row] = 1.f / s;
 }
 
 // Tile row of MFMA row m of 16-token block B.  Odd blocks use row m ^ 12 so
@@ -155,8 +109,6 @@ __device__ __forceinline__ int tile_row(int B, int m) { return 16 * B + ((B & 1)
 template <bool EXT>
 __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSLOTS * TILE_BYTES];
-  // the workgroup's 64 lo query rows (row r at r * ROWB), then 32 zero bytes
-  __shared__ __attribute__((aligned(16))) uint8_t qlo_lds[TILE_BYTES + 32];
   __shared__ float mx_lds[NWAVES][HEADS];
   __shared__ uint2 p_lds[NWAVES][2][64];
   __shared__ float l_lds[NWAVES][HEADS];
@@ -213,13 +165,12 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   };
   const uint32_t lds_tiles = (uint32_t)(uintptr_t)(
       (__attribute__((address_space(3))) uint8_t*)&kv_lds[0]);
-  // rows 8w .. 8w+7 of a 64-row block into LDS at `lds_block`: op j fills
-  // 16-byte LDS chunks 64j .. 64j+63 of the wave's block of 8 x 37 (row P /
-  // 37, chunk P % 37; the pad chunk gets a copy of chunk 35; lanes past the
-  // block masked off).  Row 8w + i comes from src + idx * 576, idx held by
-  // lane i (clamped to max_idx).
-  auto issue_rows = [&](const uint8_t* src, uint32_t max_idx, uint32_t lds_block, int32_t idx) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_block + (uint32_t)(ROWS_PER_WAVE * w * ROWB));
+  // rows 8w .. 8w+7 of a tile into a slot: op j fills 16-byte LDS chunks
+  // 64j .. 64j+63 of the wave's block of 8 x 37 (row P / 37, chunk P % 37;
+  // the pad chunk gets a copy of chunk 35; lanes past the block masked off)
+  auto issue_tile = [&](int slot, int32_t idx) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        lds_tiles + (uint32_t)(slot * TILE_BYTES + ROWS_PER_WAVE * w * ROWB));
     const int ln = opaque_lane();
 #pragma unroll
     for (int j = 0; j < DMA_OPS; ++j) {
@@ -227,57 +178,30 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       const int r = P / ROW_SLOTS;
       const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
       const uint32_t s = (uint32_t)__shfl(idx, r & 7);
-      const uint8_t* a = src + (uint64_t)(s < max_idx ? s : max_idx) * KV_WIDTH + 16 * c;
+      const uint8_t* a = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
       if (j < DMA_OPS - 1 || P < ROWS_PER_WAVE * ROW_SLOTS) issue_lds_dma16(a, base + 1024 * j);
     }
-  };
-  auto issue_tile = [&](int slot, int32_t idx) {
-    issue_rows(p.pool, p.max_slot, lds_tiles + (uint32_t)(slot * TILE_BYTES), idx);
   };
 
   // query of this wave's head group, in the d-order of the K reads: step
   // s = 2i + e, lane (t, g): q[head t][64i + 16g + 8e .. +8]
-  // query row index (query token * H + head) of workgroup row r (0..63)
-  // of request c; rows without a query map to a valid row
-  auto row_index = [&](const Cursor& c, int r) -> int64_t {
+  auto q_lane_ptr = [&](const Cursor& c) -> const uint16_t* {
     int64_t qrow = c.b;
-    int h = hs * WG_HEADS + r, k = 0;
-    if constexpr (EXT) {
-      if (p.rows_per_tok > 0) {
-        k = r / p.rows_per_tok;
-        h = r - k * p.rows_per_tok;
-      }
-      qrow = c.q_row0() + min(k, c.q_tokens() - 1);
-    }
-    return qrow * p.H + min(h, p.H - 1);
+    if constexpr (EXT) qrow = c.q_row0() + min(tk, c.q_tokens() - 1);
+    return p.q + (qrow * p.H + min(head, p.H - 1)) * KV_WIDTH + 16 * g;
   };
   // rows without a query (heads past H; extend: tokens past the block) keep a zero query
   auto row_idle = [&]() -> bool {
     if constexpr (EXT) return head >= p.H || tk >= cc.q_tokens();
     return head >= p.H;
   };
-  i32x8_t qh[Q8_CHUNKS];  // hi codes of this lane's query row, per 128-dim chunk
-  float q_inv = 1.f;      // 1 / s of this lane's row
-  const uint32_t qlo_base = (uint32_t)(uintptr_t)(
-      (__attribute__((address_space(3))) uint8_t*)&qlo_lds[0]);
-  // issue the lo query rows of request c into LDS (DMA_OPS memory ops)
-  auto issue_q = [&](const Cursor& c) {
-    const int64_t ri = row_index(c, ROWS_PER_WAVE * w + (t & 7));
-    issue_rows(p.q_lo, 0xFFFFFFFFu, qlo_base, (int32_t)ri);
-  };
-  // this wave's lo rows have landed (the caller synchronises the workgroup
-  // before they are read): load the hi codes and 1 / s of this lane's row
+  bf16x8_t qr[QSTEPS];
   auto finish_q = [&]() {
-    const int64_t ri = row_index(cc, hgl * HEADS + t);
-    const uint8_t* hp = p.q_hi + ri * KV_WIDTH;
-    const bool idle = row_idle();
+    pin_q(qr);
+    if (row_idle()) {
 #pragma unroll
-    for (int c = 0; c < Q8_CHUNKS; ++c) {
-      const int off = c < Q8_CHUNKS - 1 ? 128 * c + 32 * g : 512 + 32 * (g & 1);
-      const i32x8_t v = *reinterpret_cast<const i32x8_t*>(hp + off);
-      qh[c] = idle || (c == Q8_CHUNKS - 1 && g >= 2) ? i32x8_t{} : v;
+      for (int s = 0; s < QSTEPS; ++s) qr[s] = bf16x8_t{};
     }
-    q_inv = p.q_inv[ri];
   };
 
   // Prologue: indices of tiles 0 and 1; query, rows of tile 0, index of tile
@@ -287,9 +211,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   wait_vm<0>();
   pin(ixA);
   pin(ixB);
-  // 32 zero bytes after the lo rows (the fifth chunk's lanes g = 2, 3)
-  if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(qlo_lds + TILE_BYTES)[threadIdx.x] = 0u;
-  issue_q(cc);
+  issue_load_q(qr, q_lane_ptr(cc));
   issue_tile(0, ixA);
   ixA = load_next_index();
   if (ntiles > 1) issue_tile(1, ixB);
@@ -300,9 +222,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   // LDS offsets.  Scores: block B = 2 half + b, lane (t, g) reads chunk 4i + g
   // of tile row tile_row(B, t).  Values: as in the 16-head kernel with the
   // wave's column base 256 half.
-  const int k_row0 = tile_row(2 * half, t) * ROWB;
-  const int k_row1 = tile_row(2 * half + 1, t) * ROWB;
-  const int qlo_row = (hgl * HEADS + t) * ROWB;  // this lane's row of the lo block
+  const int k_off0 = tile_row(2 * half, t) * ROWB + 16 * g;
+  const int k_off1 = tile_row(2 * half + 1, t) * ROWB + 16 * g;
   const int tr_row0 = (t >> 1) < 4 ? 4 * g + (t >> 1) : 16 + 4 * (g ^ 3) + (t >> 1) - 4;
   const int tr_off = tr_row0 * ROWB + 8 * (t & 1) + 256 * half;
   const int s_tok0 = 32 * half + 4 * g;             // block 2 half (even)
@@ -379,33 +300,27 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     if (q_pending) {  // issued before the rows of tile k+1: those may stay in flight
       wait_vm_upto(k + 1 < ntiles ? DMA_OPS : 0);
       finish_q();
-      __syncthreads();  // every wave's lo rows landed
       q_pending = false;
     }
 
-    // a0 / c0 from the hi codes, a1 / c1 from the lo codes (weight 1/16)
     f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, c0 = a0, c1 = a0;
-    const uint8_t* kp0 = slot + k_row0;
-    const uint8_t* kp1 = slot + k_row1;
+    const uint8_t* kp0 = slot + k_off0;
+    const uint8_t* kp1 = slot + k_off1;
 #pragma unroll
-    for (int c = 0; c < Q8_CHUNKS; ++c) {
-      const int ko = c < Q8_CHUNKS - 1 ? 128 * c + 32 * g : 512 + 32 * (g & 1);
-      const i32x8_t k0 = *reinterpret_cast<const i32x8_a16_t*>(kp0 + ko);
-      const i32x8_t k1 = *reinterpret_cast<const i32x8_a16_t*>(kp1 + ko);
-      const i32x8_t ql = *reinterpret_cast<const i32x8_a16_t*>(
-          qlo_lds + (c < Q8_CHUNKS - 1 || g < 2 ? qlo_row + ko : TILE_BYTES));
-      a0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k0, qh[c], a0, 0, 0, 0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k0, ql, a1, 0, 0, 0, 0, 0, 0);
-      c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k1, qh[c], c0, 0, 0, 0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(k1, ql, c1, 0, 0, 0, 0, 0, 0);
+    for (int i = 0; i < KSTEPS; ++i) {
+      const u32x4_t kv0 = *reinterpret_cast<const u32x4_t*>(kp0 + 64 * i);
+      const u32x4_t kv1 = *reinterpret_cast<const u32x4_t*>(kp1 + 64 * i);
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[0], kv0[1]), qr[2 * i], a0, 0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[0], kv1[1]), qr[2 * i], c0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[2], kv0[3]), qr[2 * i + 1], a1, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[2], kv1[3]), qr[2 * i + 1], c1, 0, 0, 0);
     }
-    const float sc0 = p.score_scale * q_inv, sc1 = sc0 * 0.0625f;
     float s0[4], s1[4];
     float lmax = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      s0[r] = tile_lo + s_tok0 + r < tile_hi ? a0[r] * sc0 + a1[r] * sc1 : -INFINITY;
-      s1[r] = tile_lo + s_tok1 + r < tile_hi ? c0[r] * sc0 + c1[r] * sc1 : -INFINITY;
+      s0[r] = tile_lo + s_tok0 + r < tile_hi ? (a0[r] + a1[r]) * p.score_scale : -INFINITY;
+      s1[r] = tile_lo + s_tok1 + r < tile_hi ? (c0[r] + c1[r]) * p.score_scale : -INFINITY;
       lmax = fmaxf(lmax, fmaxf(s0[r], s1[r]));
     }
     lmax = wave_max_over_groups(lmax);
@@ -419,7 +334,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     Cursor nc = cc;
     if (new_q) {
       nc.advance(p, lane);
-      issue_q(nc);
+      issue_load_q(qr, q_lane_ptr(nc));
     }
     if (k + 2 < ntiles) issue_tile(slot_next2, ix_cur);
 
@@ -449,7 +364,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     p_lds[w][0][lane] = make_uint2(p01, p23);
     p_lds[w][1][lane] = make_uint2(q01, q23);
     // rows of tile k+1 landed (younger: index k+3, maybe a query, rows k+2)
-    if (k + 1 < ntiles) wait_vm_upto(1 + (new_q ? DMA_OPS : 0) + (k + 2 < ntiles ? DMA_OPS : 0));
+    if (k + 1 < ntiles) wait_vm_upto(1 + (new_q ? QSTEPS : 0) + (k + 2 < ntiles ? DMA_OPS : 0));
     __syncthreads();
 
     // P.V over the tile's 64 tokens: step st covers blocks 2st and 2st+1,
@@ -498,32 +413,17 @@ hipError_t launch_mla_decode_h64(const uint16_t* q, const uint8_t* kv_pool, int6
                                  int64_t total_tokens, int32_t batch, int32_t num_heads,
                                  float scale, float sm_scale, uint16_t* out, void* workspace,
                                  const DecodePlan& pl, hipStream_t stream) {
-  decode::SplitParams sp = make_split_params(q, kv_pool, num_slots, kv_indptr, kv_indices,
-                                             total_tokens, batch, num_heads, scale, sm_scale, out,
-                                             workspace, pl);
-  hipError_t e = launch_q_split(q, (int64_t)batch * num_heads,
-                                reinterpret_cast<char*>(workspace) + pl.q8_offset, sp, stream);
-  if (e != hipSuccess) return e;
+  const decode::SplitParams sp = make_split_params(q, kv_pool, num_slots, kv_indptr, kv_indices,
+                                                   total_tokens, batch, num_heads, scale,
+                                                   sm_scale, out, workspace, pl);
   hipLaunchKernelGGL(mla_split_h64_kernel<false>, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || total_tokens == 0) return e;
   return launch_mla_combine(sp, stream);
 }
 
 hipError_t launch_mla_split_h64_extend(const decode::SplitParams& sp, int grid, hipStream_t stream) {
   hipLaunchKernelGGL(mla_split_h64_kernel<true>, dim3(grid), dim3(THREADS), 0, stream, sp);
-  return hipGetLastError();
-}
-
-hipError_t launch_q_split(const uint16_t* q, int64_t rows, void* buffers, decode::SplitParams& sp,
-                          hipStream_t stream) {
-  const Q8Buffers qb = q8_buffers(buffers, rows);
-  sp.q_hi = qb.hi;
-  sp.q_lo = qb.lo;
-  sp.q_inv = qb.inv;
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(q_split_kernel, dim3((unsigned)((rows + QSPLIT_ROWS - 1) / QSPLIT_ROWS)),
-                     dim3(64 * QSPLIT_ROWS), 0, stream, q, rows, qb.hi, qb.lo, qb.inv);
   return hipGetLastError();
 }
 

@@ -244,8 +244,6 @@ ExtendPlan plan_mla_extend(int32_t batch, int32_t num_heads, int64_t total_q, in
   off = align256(off + 2 * ((size_t)pl.nseg + V) * pl.Hp * V_WIDTH);
   pl.lse_offset = off;
   off = align256(off + 4 * ((size_t)pl.nseg + V) * pl.Hp);
-  pl.q8_offset = off;
-  off += q8_workspace_bytes(total_q * num_heads);
   pl.workspace_bytes = off;
   return pl;
 }
@@ -292,8 +290,6 @@ hipError_t launch_mla_extend(const uint16_t* q, const uint8_t* kv_pool, int64_t 
   sp.vinfo = vinfo;
   sp.rows_per_tok = pl.rows_per_tok;
   sp.causal = causal ? 1 : 0;
-  e = launch_q_split(q, total_q * num_heads, ws + pl.q8_offset, sp, stream);
-  if (e != hipSuccess) return e;
   e = launch_mla_split_h64_extend(sp, pl.grid, stream);
   if (e != hipSuccess) return e;
 

@@ -133,3 +133,26 @@ def test_named_extend_workloads_sampled(dev, name):
     rng = np.random.default_rng(1)
     rows = np.unique(np.concatenate([[0, w.total_q - 1], rng.integers(0, w.total_q, size=12)]))
     _check(w, dev, name, rows=rows)
+
+
+@pytest.mark.parametrize("H", [256, 96])
+def test_more_than_64_heads(dev, H):
+    """Several 64-head sets per token block (H = 256: four; H = 96: two, the
+    second half empty)."""
+    w = workloads.extend(2, H, [3, 2], [150, 70], seed=H + 1)
+    _check(w, dev, "H=%d" % H)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_paged_layout(dev, causal):
+    """Slots laid out in 64-slot pages (runs of consecutive slots from scattered
+    page bases, last page partial), as in the long-context workload."""
+    w = workloads.extend(3, 16, [9, 4, 17], [200, 63, 500], page_size=64, seed=41, causal=causal)
+    _check(w, dev, "paged causal=%s" % causal)
+
+
+def test_large_scores_and_outliers(dev):
+    """Queries 4x N(0,1) over a pool with 1% +-448 outliers: near one-hot softmax."""
+    w = workloads.extend(2, 32, [5, 8], [300, 90], seed=43, q_sigma=4.0, outlier_frac=0.01,
+                         scale=2.0)
+    _check(w, dev, "outliers")
