@@ -82,11 +82,13 @@ __device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
 // lo_b = clamp(kv_indptr[b], 0, N) and hi_b = max(lo_b, clamp(kv_indptr[b+1],
 // 0, N)), and has ceil((hi_b - lo_b) / 2^SHIFT) tiles.
 template <int SHIFT>
+__device__ __forceinline__ int tiles_between(int lo, int hi) {
+  return (max(lo, hi) - lo + (1 << SHIFT) - 1) >> SHIFT;
+}
+template <int SHIFT>
 __device__ __forceinline__ int request_tiles(const int32_t* indptr, int b, int B, int N) {
   if (b >= B) return 0;
-  const int lo = clamp_tok(indptr[b], N);
-  const int hi = max(lo, clamp_tok(indptr[b + 1], N));
-  return (hi - lo + (1 << SHIFT) - 1) >> SHIFT;
+  return tiles_between<SHIFT>(clamp_tok(indptr[b], N), clamp_tok(indptr[b + 1], N));
 }
 
 // ---- the work split.  Tiles are weighted by their cost: TILE_W per tile and
@@ -105,6 +107,7 @@ struct SegmentSpan {
   int ntiles;  // tiles of this segment
   int b0, j0;  // request and tile of its first tile
   int P0;      // weight of the requests before b0
+  int win0;    // per lane: clamp(kv_indptr[min(lane, B)]), the first 64-entry window
   __device__ __forceinline__ int segment_of(int x) const { return (int)((int64_t)x * nseg / W); }
 };
 
@@ -116,9 +119,16 @@ template <int SHIFT, int THREADS, int WG_HEADS = HEADS, bool ZERO_EMPTY = true>
 __device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int hg, int lane,
                                              SegmentSpan& sp) {
   const int N = p.total_tokens;
+  // The first 64 requests' kv_indptr entries are loaded once, in one memory
+  // latency, and serve both passes and the tile cursor's first window: with
+  // at most 63 requests no other load precedes the first index load.
+  const int v0 = clamp_tok(p.indptr[min(lane, p.B)], N);
+  const int v1 = clamp_tok(p.indptr[min(lane + 1, p.B)], N);
+  const int nt0 = lane < p.B ? tiles_between<SHIFT>(v0, v1) : 0;
+  sp.win0 = v0;
   int W = 0;
   for (int c = 0; c < p.B; c += 64) {
-    const int nt = request_tiles<SHIFT>(p.indptr, c + lane, p.B, N);
+    const int nt = c == 0 ? nt0 : request_tiles<SHIFT>(p.indptr, c + lane, p.B, N);
     W += wave_sum_i32(nt > 0 ? TILE_W * nt + START_W : 0);
     uint64_t empty = seg == 0 ? __ballot(c + lane < p.B && nt == 0) : 0ull;
     while (empty) {
@@ -143,7 +153,7 @@ __device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int 
   int t0 = -1, t1 = -1, b0 = 0, j0 = 0, P0 = 0;
   int wcarry = 0, tcarry = 0;
   for (int c = 0; c < p.B && t1 < 0; c += 64) {
-    const int nt = request_tiles<SHIFT>(p.indptr, c + lane, p.B, N);
+    const int nt = c == 0 ? nt0 : request_tiles<SHIFT>(p.indptr, c + lane, p.B, N);
     const int w = nt > 0 ? TILE_W * nt + START_W : 0;
     const int Pb = wcarry + wave_inclusive_scan(w, lane) - w;
     const int TB = tcarry + wave_inclusive_scan(nt, lane) - nt;
@@ -229,6 +239,18 @@ struct TileCursor : CursorExtFields<EXT> {
     load_window(p, b0, lane);
     set_request(p, b0, lane);
     j = j0;
+  }
+  // Same, taking the window at request 0 from the segment search when it
+  // covers b0 (decode only: the extend window also carries vinfo).
+  __device__ __forceinline__ void start(const SplitParams& p, const SegmentSpan& sp, int lane) {
+    if (!EXT && sp.b0 < 63) {
+      win = 0;
+      win_val = sp.win0;
+      set_request(p, sp.b0, lane);
+      j = sp.j0;
+    } else {
+      start(p, sp.b0, sp.j0, lane);
+    }
   }
   __device__ __forceinline__ void advance(const SplitParams& p, int lane) {
     if (++j < nt) return;

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   if (!find_segment<TILE_SHIFT, THREADS>(p, seg, hg, lane, span)) return;
   const int ntiles = span.ntiles;
   TileCursor<TILE_SHIFT> cc;  // tile being computed
-  cc.start(p, span.b0, span.j0, lane);
+  cc.start(p, span, lane);
   TileCursor<TILE_SHIFT> lc = cc;  // next tile whose index is loaded
 
   // ---- row tiles.  Tile k of the segment goes to LDS slot k & 1 by

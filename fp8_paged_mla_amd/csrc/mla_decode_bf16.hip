@@ -69,7 +69,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_bf16_kernel(const SplitPara
   if (!find_segment<TILE_SHIFT, THREADS>(p, seg, hg, lane, span)) return;
   const int ntiles = span.ntiles;
   TileCursor<TILE_SHIFT> cc;
-  cc.start(p, span.b0, span.j0, lane);
+  cc.start(p, span, lane);
   TileCursor<TILE_SHIFT> lc = cc;
 
   // index of the load cursor's tile (lane r < 16 and its copies: token

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   const int ntiles = span.ntiles;
   using Cursor = TileCursor<TILE_SHIFT, EXT>;
   Cursor cc;
-  cc.start(p, span.b0, span.j0, lane);
+  cc.start(p, span, lane);
   Cursor lc = cc;
 
   auto opaque_lane = [&]() -> int {
