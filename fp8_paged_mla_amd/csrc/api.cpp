@@ -144,8 +144,8 @@ int mla_extend_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
 }
 
 size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens) {
-  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_tokens < 0 ||
-      total_tokens > kMaxTokens)
+  if (batch < 1 || batch > FP8MLA_MAX_BATCH || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS ||
+      total_tokens < 0 || total_tokens > kMaxTokens)
     return 0;
   if (total_tokens == 0) return 0;
   const int cus = current_device_cus();
@@ -159,8 +159,8 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
                    const int32_t* kv_indptr, const int32_t* kv_indices, int64_t total_tokens,
                    int32_t batch, int32_t num_heads, float scale, float sm_scale, uint16_t* out,
                    void* workspace, size_t workspace_bytes, void* stream) {
-  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_tokens < 0 ||
-      total_tokens > kMaxTokens || num_slots < 0 || num_slots > kMaxSlots)
+  if (batch < 1 || batch > FP8MLA_MAX_BATCH || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS ||
+      total_tokens < 0 || total_tokens > kMaxTokens || num_slots < 0 || num_slots > kMaxSlots)
     return FP8MLA_ERR_BAD_SHAPE;
   if (total_tokens > 0 && num_slots == 0) return FP8MLA_ERR_BAD_SHAPE;
   if (!isfinite(scale) || !(scale > 0.0f) || !isfinite(sm_scale)) return FP8MLA_ERR_BAD_SCALAR;
@@ -182,8 +182,8 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
 }
 
 size_t mla_decode_bf16_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens) {
-  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_tokens < 0 ||
-      total_tokens > kMaxTokens)
+  if (batch < 1 || batch > FP8MLA_MAX_BATCH || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS ||
+      total_tokens < 0 || total_tokens > kMaxTokens)
     return 0;
   if (total_tokens == 0) return 0;
   const int cus = current_device_cus();
@@ -196,8 +196,8 @@ int mla_decode_bf16(const uint16_t* q, const uint16_t* kv, int64_t num_rows,
                     const int32_t* kv_indptr, const int32_t* kv_indices, int64_t total_tokens,
                     int32_t batch, int32_t num_heads, float scale, float sm_scale, uint16_t* out,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_tokens < 0 ||
-      total_tokens > kMaxTokens || num_rows < 0 || num_rows > kMaxSlots)
+  if (batch < 1 || batch > FP8MLA_MAX_BATCH || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS ||
+      total_tokens < 0 || total_tokens > kMaxTokens || num_rows < 0 || num_rows > kMaxSlots)
     return FP8MLA_ERR_BAD_SHAPE;
   if (total_tokens > 0 && num_rows == 0) return FP8MLA_ERR_BAD_SHAPE;
   if (!isfinite(scale) || !(scale > 0.0f) || !isfinite(sm_scale)) return FP8MLA_ERR_BAD_SCALAR;

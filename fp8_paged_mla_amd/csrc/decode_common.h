@@ -99,8 +99,9 @@ __device__ __forceinline__ int request_tiles(const int32_t* indptr, int b, int B
 // / n)), W the total weight, so tile x belongs to segment floor(x n / W).
 // Consecutive tile positions are at most TILE_W + START_W apart, so with at
 // most W / (TILE_W + START_W) segments every segment holds a tile and the
-// pieces of a request are consecutive segments.  (Weights fit in int:
-// W <= 4 (N + B) + 2 B.)
+// pieces of a request are consecutive segments.  (Weights fit in int: with
+// tiles of at least 64 tokens W <= 4 (N / 64 + B) + 2 B < 2^31 for
+// N < 2^31 and B <= 2^24, the batch limit the host enforces.)
 struct SegmentSpan {
   int nseg;    // segments in use
   int W;       // total weight

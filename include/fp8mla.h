@@ -50,6 +50,7 @@ extern "C" {
 #define FP8MLA_KV_WIDTH 576   /* latent row: 512 latent + 64 rope           */
 #define FP8MLA_V_WIDTH 512    /* value operand = first 512 columns of a row */
 #define FP8MLA_MAX_HEADS 256  /* query heads sharing the single KV head     */
+#define FP8MLA_MAX_BATCH (1 << 24) /* requests per decode call                */
 
 /* Status codes (0 = success, negative = error). */
 #define FP8MLA_OK 0
@@ -151,8 +152,8 @@ int scatter_cast_bf16_fp8(const uint16_t* src, int64_t n, int64_t src_row_stride
  *               are garbage afterwards.  Calls that may overlap (different
  *               streams) need different workspaces.  May be NULL when
  *               total_tokens == 0.
- *   1 <= batch, 1 <= num_heads <= FP8MLA_MAX_HEADS, total_tokens >= 0,
- *   num_slots >= 1 (unless total_tokens == 0).
+ *   1 <= batch <= FP8MLA_MAX_BATCH, 1 <= num_heads <= FP8MLA_MAX_HEADS,
+ *   total_tokens >= 0, num_slots >= 1 (unless total_tokens == 0).
  * Each request's tokens are cut into 128-token tiles; the list of all tiles
  * is split into equal segments over the compute units (flash-decoding
  * split-K), and a second kernel merges the pieces of requests that span

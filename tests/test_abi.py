@@ -134,6 +134,7 @@ def _decode(lib, **kw):
 def test_mla_decode_validation():
     lib = _lib()
     assert _decode(lib, B=0) == ERR_SHAPE
+    assert _decode(lib, B=(1 << 24) + 1) == ERR_SHAPE  # FP8MLA_MAX_BATCH: the split's weights stay in int
     assert _decode(lib, H=0) == ERR_SHAPE
     assert _decode(lib, H=257) == ERR_SHAPE
     assert _decode(lib, total=-1) == ERR_SHAPE
@@ -171,6 +172,7 @@ def test_mla_decode_bf16_validation():
                                    a["ws"], a["ws_bytes"], a["stream"])
 
     assert dec(B=0) == ERR_SHAPE
+    assert dec(B=(1 << 24) + 1) == ERR_SHAPE
     assert dec(H=257) == ERR_SHAPE
     assert dec(rows=0) == ERR_SHAPE
     assert dec(total=-1) == ERR_SHAPE
@@ -185,6 +187,7 @@ def test_mla_decode_bf16_validation():
 def test_workspace_query_rejects_bad_sizes():
     lib = _lib()
     assert lib.mla_decode_fp8_workspace_bytes(0, 16, 10) == 0
+    assert lib.mla_decode_fp8_workspace_bytes((1 << 24) + 1, 16, 10) == 0
     assert lib.mla_decode_fp8_workspace_bytes(1, 0, 10) == 0
     assert lib.mla_decode_fp8_workspace_bytes(1, 300, 10) == 0
     assert lib.mla_decode_fp8_workspace_bytes(1, 16, -1) == 0
