@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -65,11 +66,20 @@ def parse_args():
     return ap.parse_args()
 
 
+def _code_only(text):
+    """C/C++ source with comments removed and whitespace runs collapsed, so
+    that the digest below changes with the code and not with its comments
+    (string literals in these sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(paths):
     h = hashlib.sha256()
     for path in paths:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
