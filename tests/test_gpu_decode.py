@@ -52,6 +52,20 @@ def test_ragged_lengths(dev, lengths):
     _check_full(w, str(lengths))
 
 
+# Many short requests: segments start at nearly every request index, on
+# both sides of the first 64-entry kv_indptr window that the segment search
+# hands to the tile cursor (segments start at requests 62, 63 and 65; request
+# 64 is empty, so the cursor steps over it from 63).
+@pytest.mark.parametrize("seed", [0, 1])
+def test_many_requests_across_indptr_windows(dev, seed):
+    rng = np.random.default_rng(700 + seed)
+    lengths = [int(x) for x in rng.integers(1, 200, size=200)]
+    lengths[64] = 0
+    lengths[130] = 0
+    w = workloads.small(len(lengths), 16, lengths, seed=seed, device=dev)
+    _check_full(w, "B=200 seed %d" % seed)
+
+
 # 64 or more heads with enough tokens (at least 4 64-token tiles per
 # workgroup slot: 4 * CUs / ceil(H / 64) tiles) run the 64-heads-per-workgroup
 # kernel.  Sizes just above that threshold cover padding (80 = 64 + 16),
