@@ -325,7 +325,7 @@ def cast_path_step(fm, workloads, torch, dev, args):
     gather_path_ms = timed(gather_path)
     cast_bytes = 495552 * 576 * 3
     gather_bytes = w0.total_tokens * (4 + 576 + 1152)
-    return {
+    result = {
         "metric": "per-decode-step time over %d layers: full-pool cast vs gather-cast vs fused" % L,
         "unit": "ms/step",
         "higher_is_better": False,
@@ -345,6 +345,33 @@ def cast_path_step(fm, workloads, torch, dev, args):
         "gather_then_attend_us_per_layer": round(gather_path_ms * 1e3 / L, 2),
         "fused_speedup_vs_cast_then_attend": round(cast_path_ms / fused_ms, 1),
         "fused_speedup_vs_gather_then_attend": round(gather_path_ms / fused_ms, 2),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_cast_baseline(pools[0], L)
+    return result
+
+
+def cpu_cast_baseline(pool, layers, budget_s=10.0):
+    """The oracle's full-pool cast (a 256-entry table lookup in numpy, one
+    thread) of one 495,552-slot pool on the host, repeated for about budget_s
+    seconds; the per-step figure multiplies the per-pool time by the layer
+    count (layers x pool and BF16 copy would not fit in host memory)."""
+    import oracle
+    host = pool.cpu().numpy()
+    reps = 0
+    t0 = time.perf_counter()
+    while reps == 0 or time.perf_counter() - t0 < budget_s:
+        oracle.cast_ref(host)
+        reps += 1
+    per_pool_s = (time.perf_counter() - t0) / reps
+    return {
+        "value": round(per_pool_s * layers * 1e3, 1),
+        "unit": "ms/step",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "oracle cast (numpy table lookup) of one %d-slot pool (%.0f MB) on one "
+                  "host thread, %d repetitions at %.3f s each, times %d layers "
+                  "(extrapolated)" % (host.shape[0], host.nbytes / 1e6, reps, per_pool_s, layers),
     }
 
 
