@@ -76,8 +76,10 @@ int gather_cast_fp8_bf16(const uint8_t* pool, int64_t num_slots, const int32_t* 
   if (num_slots == 0) return FP8MLA_ERR_BAD_SHAPE;
   if (!pool || !indices || !out) return FP8MLA_ERR_NULL_PTR;
   if (!aligned16(pool) || !aligned16(out) || !aligned4(indices)) return FP8MLA_ERR_MISALIGNED;
+  const int cus = current_device_cus();
+  if (cus <= 0) return FP8MLA_ERR_HIP;
   const hipError_t e = fp8mla::launch_gather_cast(pool, num_slots, indices, n, out,
-                                                  static_cast<hipStream_t>(stream));
+                                                  static_cast<hipStream_t>(stream), cus);
   return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
 }
 

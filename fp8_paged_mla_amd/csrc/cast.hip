@@ -3,10 +3,10 @@
 //
 // Both are pure bandwidth work (1 byte read, 2 bytes written per element, plus
 // 4 index bytes per gathered row), so they are written for coalescing, not
-// for arithmetic: 8-byte loads and 16-byte stores per lane that make every
-// wave instruction one contiguous span, several loads in flight per lane, and
-// one conversion instruction per two elements.
-#include "device_common.h"
+// for arithmetic: every wave instruction covers one contiguous span, several
+// loads are in flight per lane, and one conversion instruction handles two
+// elements.
+#include "decode_common.h"  // global->LDS copies and explicit vmcnt waits
 #include "launch.h"
 
 namespace fp8mla {
@@ -38,65 +38,231 @@ __device__ __forceinline__ u32x4_t convert8(const u32x2_t in) {
   return o;
 }
 
-constexpr int CAST_THREADS = 256;
-constexpr int CAST_UNROLL = 8;
-constexpr int CAST_BLOCKS_PER_CU = 32;
+// Full-pool cast.  The input reaches LDS by global->LDS copies, which keep
+// more bytes in flight per CU than register loads do (no registers wait on
+// them): each wave cycles through CAST_SLOTS private LDS slots of one
+// 2 KB chunk each, copying chunk k + CAST_SLOTS while it converts and
+// stores chunk k.  Chunks are dealt to waves grid-stride; lane l copies bytes
+// 16l..16l+15 of each KB of the chunk and then reads back 8-byte pieces
+// 512h + 8l (h = 0..3), so every store instruction writes 1 KB of
+// contiguous BF16.  Only the issuing wave reads its slots, so an explicit
+// vmcnt wait orders the copy before the reads.  The bytes past the last
+// whole chunk are cast by the register path below.  One workgroup of four
+// waves per CU with 4 KB in flight per wave measured fastest on MI355X.
+constexpr int CAST_WAVES = 4;
+constexpr int CAST_THREADS = 64 * CAST_WAVES;
+constexpr int CAST_SLOTS = 2;
+constexpr int CAST_CHUNK = 2048;                 // input bytes per chunk: two 1 KB copy ops
+constexpr int CAST_OPS = CAST_CHUNK / 1024;
 
-// Grid-stride over 8-byte input chunks: lane i reads bytes 8i..8i+7 and
-// writes output bytes 16i..16i+15, so every load and store instruction of a
-// wave covers one contiguous span (512 B in, 1 KB out).  Stores that leave
-// half-written lines behind (two 16-byte stores per lane at a 32-byte
-// stride) cost about a quarter more HBM write traffic on this part.  Each
-// lane keeps CAST_UNROLL loads in flight; accesses are non-temporal since
-// pool and copy are streamed once.
-__global__ __launch_bounds__(CAST_THREADS) void cast_pool_kernel(const u32x2_t* __restrict__ in,
-                                                                 u32x4_t* __restrict__ out,
-                                                                 int64_t n8) {
-  const int64_t stride = (int64_t)gridDim.x * CAST_THREADS;
-  int64_t i = (int64_t)blockIdx.x * CAST_THREADS + threadIdx.x;
-  for (; i + (CAST_UNROLL - 1) * stride < n8; i += CAST_UNROLL * stride) {
-    u32x2_t v[CAST_UNROLL];
-#pragma unroll
-    for (int u = 0; u < CAST_UNROLL; ++u) v[u] = load8_nt(&in[i + u * stride]);
-#pragma unroll
-    for (int u = 0; u < CAST_UNROLL; ++u) store16_nt(&out[i + u * stride], convert8(v[u]));
-  }
-  for (; i < n8; i += stride) store16_nt(&out[i], convert8(load8_nt(&in[i])));
+// Wait until chunk k of a wave's list (of K) has landed.  Issue order: the
+// prologue copies chunks 0..P0-1 (P0 = min(K, CAST_SLOTS)); iteration j then
+// issues the copies of chunk j + CAST_SLOTS (if any) and 2 * CAST_OPS stores,
+// and stores count in vmcnt too.  The number of operations younger than
+// chunk k's last copy is therefore
+//   k < S:  OPS (P0 - 1 - k) + 3 OPS k - OPS m,
+//   k >= S: 3 OPS (S - 1) + 2 OPS - OPS m,    m = #{j < k : j + S >= K},
+// and waiting for at most the largest immediate below that count proves the
+// chunk complete (a smaller immediate only waits longer).
+__device__ __forceinline__ void cast_wait_chunk(int64_t k, int64_t K) {
+  constexpr int S = CAST_SLOTS, OPS = CAST_OPS;
+  const int64_t P0 = K < S ? K : S;
+  const int64_t tail_start = K - S > 0 ? K - S : 0;
+  const int64_t m = k > tail_start ? k - tail_start : 0;
+  const int64_t younger = k < S ? OPS * (P0 - 1 - k) + 3 * OPS * k - OPS * m
+                                : 3 * OPS * (S - 1) + 2 * OPS - OPS * m;
+  using decode::wait_vm;
+  if (younger >= 10) wait_vm<10>();
+  else if (younger >= 8) wait_vm<8>();
+  else if (younger >= 6) wait_vm<6>();
+  else if (younger >= 4) wait_vm<4>();
+  else if (younger >= 2) wait_vm<2>();
+  else if (younger >= 1) wait_vm<1>();
+  else wait_vm<0>();
 }
 
-// Gather-then-cast: one block of 576 lanes covers 8 rows per pass (72 lanes
-// x 8 bytes per row) and GATHER_UNROLL passes, i.e. 64 consecutive output
-// rows.  Lanes of a row read its 576 contiguous bytes; the block's output
-// rows are contiguous, 16 bytes per lane.
-constexpr int GATHER_LANES_PER_ROW = KV_WIDTH / 8;                       // 72
-constexpr int GATHER_ROWS_PER_PASS = 8;
-constexpr int GATHER_THREADS = GATHER_ROWS_PER_PASS * GATHER_LANES_PER_ROW;  // 576 = 9 waves
-constexpr int GATHER_UNROLL = 8;
-constexpr int GATHER_ROWS_PER_BLOCK = GATHER_ROWS_PER_PASS * GATHER_UNROLL;  // 64
+__global__ __launch_bounds__(CAST_THREADS) void cast_pool_kernel(const uint8_t* __restrict__ in,
+                                                                 u32x4_t* __restrict__ out,
+                                                                 int64_t nbytes) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring[CAST_WAVES][CAST_SLOTS][CAST_CHUNK];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nchunks = nbytes / CAST_CHUNK;
+  const int64_t gw = (int64_t)blockIdx.x * CAST_WAVES + w, nw = (int64_t)gridDim.x * CAST_WAVES;
+  const int64_t K = gw < nchunks ? (nchunks - gw + nw - 1) / nw : 0;  // this wave's chunks
+  const uint32_t base = (uint32_t)(uintptr_t)(
+      (__attribute__((address_space(3))) uint8_t*)&ring[w][0][0]);
+  auto issue_chunk = [&](int64_t k, int slot) {
+    const uint8_t* src = in + (gw + k * nw) * CAST_CHUNK + 16 * lane;
+#pragma unroll
+    for (int o = 0; o < CAST_OPS; ++o)
+      decode::issue_lds_dma16(src + 1024 * o,
+                              __builtin_amdgcn_readfirstlane(base + CAST_CHUNK * slot + 1024 * o));
+  };
+  for (int d = 0; d < CAST_SLOTS; ++d)
+    if (d < K) issue_chunk(d, d);
+  for (int64_t k = 0; k < K; ++k) {
+    cast_wait_chunk(k, K);
+    const int slot = (int)(k % CAST_SLOTS);
+    u32x2_t v[2 * CAST_OPS];
+#pragma unroll
+    for (int h = 0; h < 2 * CAST_OPS; ++h)
+      v[h] = *reinterpret_cast<const u32x2_t*>(&ring[w][slot][512 * h + 8 * lane]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot is read before it is refilled
+    if (k + CAST_SLOTS < K) issue_chunk(k + CAST_SLOTS, slot);
+    u32x4_t* dst = out + (gw + k * nw) * (CAST_CHUNK / 8) + lane;
+#pragma unroll
+    for (int h = 0; h < 2 * CAST_OPS; ++h) store16_nt(dst + 64 * h, convert8(v[h]));
+  }
+  decode::wait_vm<0>();
+  // the bytes past the last whole chunk, 8 per lane, grid-stride
+  const int64_t stride = (int64_t)gridDim.x * CAST_THREADS;
+  for (int64_t i = nchunks * (CAST_CHUNK / 8) + (int64_t)blockIdx.x * CAST_THREADS + threadIdx.x;
+       i < nbytes / 8; i += stride)
+    store16_nt(&out[i], convert8(load8_nt(in + 8 * i)));
+}
+
+// Gather-then-cast.  Output rows go to waves in chunks of 16 consecutive
+// rows (9 KB of FP8 in, 18 KB of BF16 out), grid-stride.  A chunk's slot ids
+// and rows reach LDS by global->LDS copies: 64 bytes of ids into a small
+// per-wave id ring, then 9 copy ops of 1 KB in which lane l of op j takes
+// 16-byte piece P = 64j + l of the chunk (row P / 36, piece P % 36), so every
+// op reads whole rows back to back.  The chunk is then read back linearly,
+// 8 bytes per lane, converted and written with 18 contiguous 1 KB stores.
+// Each wave keeps GATHER_SLOTS chunks in flight; the ids of chunk k + S + 1
+// are copied one iteration before that chunk's rows.  No register is ever the
+// destination of a load in flight.  Rows past the last whole chunk are cast
+// by the register path below.
+constexpr int GATHER_WAVES = 4;
+constexpr int GATHER_THREADS = 64 * GATHER_WAVES;
+constexpr int GATHER_SLOTS = 3;
+constexpr int GATHER_ROWS = 16;                                 // rows per chunk
+constexpr int GATHER_OPS = GATHER_ROWS * KV_WIDTH / 1024;       // 9 copy ops of 1 KB
+constexpr int GATHER_STORES = GATHER_ROWS * KV_WIDTH * 2 / 1024;  // 18 stores of 1 KB
+constexpr int GATHER_ID_SLOTS = GATHER_SLOTS + 2;
+static_assert(GATHER_ROWS * KV_WIDTH == GATHER_OPS * 1024, "chunk is whole 1 KB copy ops");
+
+__device__ __forceinline__ void issue_lds_dma4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// Issue order of a wave with K chunks (S = GATHER_SLOTS, G = GATHER_OPS,
+// R = GATHER_STORES): A = min(K, S + 1) id copies, one drain, the row copies of
+// chunks 0..P0-1 (P0 = min(K, S)); then iteration j issues [ids of chunk
+// j + S + 1, if any] [rows of chunk j + S, if any] [R stores].  With
+// T(k) = T0 + sum over j < k of the ops of iteration j, waiting for at most
+// min(younger than chunk k's last row copy, younger than chunk k + S's id
+// copy) operations proves both complete (stores count in vmcnt too).
+__device__ __forceinline__ void gather_wait_chunk(int64_t k, int64_t K) {
+  constexpr int S = GATHER_SLOTS, G = GATHER_OPS, R = GATHER_STORES;
+  const int64_t A = K < S + 1 ? K : S + 1;
+  const int64_t P0 = K < S ? K : S;
+  const int64_t T0 = A + G * P0;
+  const int64_t KS = K - S > 0 ? K - S : 0, KS1 = K - S - 1 > 0 ? K - S - 1 : 0;
+  auto ops_before = [&](int64_t i) -> int64_t {  // ops of iterations 0..i-1
+    return R * i + G * (i < KS ? i : KS) + (i < KS1 ? i : KS1);
+  };
+  const int64_t Tk = T0 + ops_before(k);
+  int64_t last_row_copy;
+  if (k < P0) {
+    last_row_copy = A + G * k + G - 1;
+  } else {
+    const int64_t j = k - S;
+    last_row_copy = T0 + ops_before(j) + (j + S + 1 < K ? 1 : 0) + G - 1;
+  }
+  int64_t younger = Tk - last_row_copy - 1;
+  if (k + S < K) {
+    const int64_t id_copy = k == 0 ? S : T0 + ops_before(k - 1);
+    const int64_t y = Tk - id_copy - 1;
+    younger = y < younger ? y : younger;
+  }
+  using decode::wait_vm;
+  if (younger >= 48) wait_vm<48>();
+  else if (younger >= 40) wait_vm<40>();
+  else if (younger >= 32) wait_vm<32>();
+  else if (younger >= 27) wait_vm<27>();
+  else if (younger >= 24) wait_vm<24>();
+  else if (younger >= 18) wait_vm<18>();
+  else if (younger >= 12) wait_vm<12>();
+  else if (younger >= 9) wait_vm<9>();
+  else if (younger >= 4) wait_vm<4>();
+  else if (younger >= 1) wait_vm<1>();
+  else wait_vm<0>();
+}
 
 __global__ __launch_bounds__(GATHER_THREADS) void gather_cast_kernel(
     const uint8_t* __restrict__ pool, uint32_t max_slot, const int32_t* __restrict__ indices,
     int64_t n, u32x4_t* __restrict__ out) {
-  const int rr = threadIdx.x / GATHER_LANES_PER_ROW;
-  const int c = threadIdx.x - rr * GATHER_LANES_PER_ROW;
-  const int64_t r0 = (int64_t)blockIdx.x * GATHER_ROWS_PER_BLOCK + rr;
-  uint32_t slot[GATHER_UNROLL];
+  constexpr int S = GATHER_SLOTS;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[GATHER_WAVES][S][GATHER_OPS * 1024];
+  __shared__ __attribute__((aligned(16))) int32_t id_ring[GATHER_WAVES][GATHER_ID_SLOTS][64];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t nchunks = n / GATHER_ROWS;
+  const int64_t gw = (int64_t)blockIdx.x * GATHER_WAVES + w, nw = (int64_t)gridDim.x * GATHER_WAVES;
+  const int64_t K = gw < nchunks ? (nchunks - gw + nw - 1) / nw : 0;  // this wave's chunks
+  const uint32_t rows_base = (uint32_t)(uintptr_t)(
+      (__attribute__((address_space(3))) uint8_t*)&ring[w][0][0]);
+  const uint32_t ids_base = (uint32_t)(uintptr_t)(
+      (__attribute__((address_space(3))) int32_t*)&id_ring[w][0][0]);
+  // slot ids of chunk k (lane l copies row l & 15) into id slot k % GATHER_ID_SLOTS
+  auto copy_ids = [&](int64_t k) -> int {
+    const int slot = (int)(k % GATHER_ID_SLOTS);
+    issue_lds_dma4(indices + (gw + k * nw) * GATHER_ROWS + (lane & 15),
+                   __builtin_amdgcn_readfirstlane(ids_base + 256 * slot));
+    return slot;
+  };
+  auto copy_rows = [&](int id_slot, int slot) {
 #pragma unroll
-  for (int u = 0; u < GATHER_UNROLL; ++u) {
-    const int64_t r = r0 + u * GATHER_ROWS_PER_PASS;
-    const uint32_t s = r < n ? (uint32_t)indices[r] : 0u;
-    slot[u] = s < max_slot ? s : max_slot;  // negative or too large -> last slot
+    for (int j = 0; j < GATHER_OPS; ++j) {
+      const int P = 64 * j + lane;
+      const int r = P / KV_CHUNKS;
+      const uint32_t s = (uint32_t)id_ring[w][id_slot][r];  // negative ids compare as large
+      const uint8_t* src = pool + (uint64_t)(s < max_slot ? s : max_slot) * KV_WIDTH +
+                           16 * (P - KV_CHUNKS * r);
+      decode::issue_lds_dma16(src, __builtin_amdgcn_readfirstlane(
+                                       rows_base + GATHER_OPS * 1024 * slot + 1024 * j));
+    }
+  };
+
+  const int64_t A = K < S + 1 ? K : S + 1;
+  const int64_t P0 = K < S ? K : S;
+  int id_slot[S + 1];
+#pragma unroll
+  for (int d = 0; d <= S; ++d) id_slot[d] = d < A ? copy_ids(d) : 0;
+  decode::wait_vm<0>();
+#pragma unroll
+  for (int d = 0; d < S; ++d)
+    if (d < P0) copy_rows(id_slot[d], d);
+  int ids_next = id_slot[S];
+  for (int64_t k = 0; k < K; ++k) {
+    gather_wait_chunk(k, K);
+    const int slot = (int)(k % S);
+    u32x2_t v[GATHER_STORES];
+#pragma unroll
+    for (int h = 0; h < GATHER_STORES; ++h)
+      v[h] = *reinterpret_cast<const u32x2_t*>(&ring[w][slot][512 * h + 8 * lane]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot is read before it is refilled
+    if (k + S < K) {
+      const int ids = ids_next;
+      if (k + S + 1 < K) ids_next = copy_ids(k + S + 1);
+      copy_rows(ids, slot);
+    }
+    u32x4_t* dst = out + (gw + k * nw) * GATHER_ROWS * (KV_WIDTH / 8) + lane;
+#pragma unroll
+    for (int h = 0; h < GATHER_STORES; ++h) store16_nt(dst + 64 * h, convert8(v[h]));
   }
-  u32x2_t v[GATHER_UNROLL];
-#pragma unroll
-  for (int u = 0; u < GATHER_UNROLL; ++u) {
-    const int64_t r = r0 + u * GATHER_ROWS_PER_PASS;
-    if (r < n) v[u] = load8_nt(pool + (uint64_t)slot[u] * KV_WIDTH + 8 * c);
-  }
-#pragma unroll
-  for (int u = 0; u < GATHER_UNROLL; ++u) {
-    const int64_t r = r0 + u * GATHER_ROWS_PER_PASS;
-    if (r < n) store16_nt(&out[r * GATHER_LANES_PER_ROW + c], convert8(v[u]));
+  decode::wait_vm<0>();
+  // rows past the last whole chunk, 8 bytes per lane
+  const int64_t first = nchunks * GATHER_ROWS * (KV_WIDTH / 8);
+  const int64_t total = n * (KV_WIDTH / 8);
+  for (int64_t e = first + (int64_t)blockIdx.x * GATHER_THREADS + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * GATHER_THREADS) {
+    const int64_t r = e / (KV_WIDTH / 8);
+    const int c = (int)(e - r * (KV_WIDTH / 8));
+    const uint32_t s = (uint32_t)indices[r];
+    store16_nt(&out[e], convert8(load8_nt(pool + (uint64_t)(s < max_slot ? s : max_slot) * KV_WIDTH + 8 * c)));
   }
 }
 
@@ -104,20 +270,24 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_cast_kernel(
 
 hipError_t launch_cast_pool(const uint8_t* pool, int64_t num_slots, uint16_t* out,
                             hipStream_t stream, int num_cus) {
-  const int64_t n8 = num_slots * (KV_WIDTH / 8);
-  if (n8 == 0) return hipSuccess;
-  int64_t blocks = (n8 + CAST_THREADS - 1) / CAST_THREADS;
-  const int64_t cap = (int64_t)num_cus * CAST_BLOCKS_PER_CU;
-  if (blocks > cap) blocks = cap;
+  const int64_t nbytes = num_slots * KV_WIDTH;  // a multiple of 64
+  if (nbytes == 0) return hipSuccess;
+  // one workgroup per CU (fewer for pools of fewer chunks than waves)
+  const int64_t waves_needed = nbytes / CAST_CHUNK + 1;
+  int64_t blocks = (waves_needed + CAST_WAVES - 1) / CAST_WAVES;
+  if (blocks > num_cus) blocks = num_cus;
   hipLaunchKernelGGL(cast_pool_kernel, dim3((unsigned)blocks), dim3(CAST_THREADS), 0, stream,
-                     reinterpret_cast<const u32x2_t*>(pool), reinterpret_cast<u32x4_t*>(out), n8);
+                     pool, reinterpret_cast<u32x4_t*>(out), nbytes);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_cast(const uint8_t* pool, int64_t num_slots, const int32_t* indices,
-                              int64_t n, uint16_t* out, hipStream_t stream) {
+                              int64_t n, uint16_t* out, hipStream_t stream, int num_cus) {
   if (n == 0) return hipSuccess;
-  const int64_t blocks = (n + GATHER_ROWS_PER_BLOCK - 1) / GATHER_ROWS_PER_BLOCK;
+  // one workgroup per CU (fewer when there are fewer chunks than waves)
+  const int64_t waves_needed = n / GATHER_ROWS + 1;
+  int64_t blocks = (waves_needed + GATHER_WAVES - 1) / GATHER_WAVES;
+  if (blocks > num_cus) blocks = num_cus;
   hipLaunchKernelGGL(gather_cast_kernel, dim3((unsigned)blocks), dim3(GATHER_THREADS), 0, stream,
                      pool, (uint32_t)(num_slots - 1), indices, n, reinterpret_cast<u32x4_t*>(out));
   return hipGetLastError();

@@ -12,7 +12,8 @@ hipError_t launch_cast_pool(const uint8_t* pool, int64_t num_slots, uint16_t* ou
                             hipStream_t stream, int num_cus);
 
 hipError_t launch_gather_cast(const uint8_t* pool, int64_t num_slots, const int32_t* indices,
-                              int64_t n, uint16_t* out, hipStream_t stream);
+                              int64_t n, uint16_t* out, hipStream_t stream,
+                              int num_cus);
 
 hipError_t launch_scatter_cast(const uint16_t* src, int64_t src_row_stride, int64_t n,
                                const int32_t* slots, uint8_t* pool, int64_t num_slots,

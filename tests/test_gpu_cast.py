@@ -24,7 +24,9 @@ def _all_codes_pool(rows):
     return torch.from_numpy(codes.astype(np.uint8).reshape(rows, 576))
 
 
-@pytest.mark.parametrize("rows", [1, 3, 4, 37, 1000])
+# 1-3 rows: less than one 2 KB chunk; 4, 37, 1000: a few chunks and a tail;
+# 100003: 27-28 chunks per wave over 1,024 waves and a 1,728-byte tail
+@pytest.mark.parametrize("rows", [1, 3, 4, 37, 1000, 100003])
 def test_cast_pool_all_codes(dev, rows):
     pool = _all_codes_pool(rows)
     out = fm.cast_pool_fp8_bf16(pool.to(dev))
