@@ -181,7 +181,14 @@ struct ExtendCombineParams {
 // token get zero rows; the rest merge their pieces.
 __global__ __launch_bounds__(64 * COMBINE_ROWS) void extend_combine_kernel(const ExtendCombineParams p) {
   const int v = blockIdx.x;
-  if (v >= p.hdr[0]) return;
+  // The count, the block's vinfo and its piece range are loaded together (one
+  // memory latency): vinfo and pieces hold vmax = gridDim.x entries, so the
+  // reads are in bounds for every block; past the count they are not used.
+  const int count = p.hdr[0];
+  const int2 vi = p.vinfo[v];
+  const int2 rp = p.pieces[v];
+  asm volatile("" ::"s"(count), "s"(vi.x), "s"(vi.y), "s"(rp.x), "s"(rp.y));  // all three issued here
+  if (v >= count) return;
   const int row = blockIdx.y * COMBINE_ROWS + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   int tk = 0, head = row;
@@ -189,9 +196,7 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void extend_combine_kernel(const
     tk = row / p.rows_per_tok;
     head = row - tk * p.rows_per_tok;
   }
-  const int2 vi = p.vinfo[v];
   if (head >= p.H || tk > (vi.y >> kExtQ0Bits)) return;
-  const int2 rp = p.pieces[v];
   if (rp.y == 1) return;
   uint16_t* op = p.out + ((int64_t)((vi.y & kExtQ0Mask) + tk) * p.H + head) * V_WIDTH;
   if (rp.y == 0) {
