@@ -45,6 +45,15 @@ struct SplitParams {
   int32_t causal;
 };
 
+// P.V runs in FP16 (the FP16 MFMA is as fast as the BF16 one): the E4M3
+// values are exact in FP16, and a probability keeps 11 significant bits
+// instead of BF16's 8, so that values of opposite sign up to 448 that cancel
+// leave a rounding error well inside the tolerance.  Probabilities are
+// formed as exp2(s - m + kPScaleLog2), i.e. scaled by 2^15 into [0, 2^15], so
+// that they stay normal FP16 numbers down to 2^-29 of the row maximum; the
+// scale cancels in O / l and is taken out of the log-sum-exp of a partial.
+constexpr float kPScaleLog2 = 15.0f;
+
 constexpr int kExtQ0Bits = 29;                 // first query row in the low 29 bits of vinfo.y
 constexpr int kExtQ0Mask = (1 << kExtQ0Bits) - 1;
 
@@ -300,8 +309,6 @@ __device__ __forceinline__ void pin(int32_t& x) { asm volatile("" : "+v"(x)); }
 // hold E4M3 values (|v| <= 448), so the partials, convex combinations of
 // them, cannot overflow, and fp16's 11-bit significand is finer than the
 // bf16 the merged output is rounded to.
-typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
-
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   const f16x2_t v = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, v);

@@ -8,6 +8,8 @@ namespace fp8mla {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) int i32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
@@ -36,6 +38,22 @@ __device__ __forceinline__ bf16x8_t e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   v[2] = e4m3x2_to_bf16x2<false>(hi);
   v[3] = e4m3x2_to_bf16x2<true>(hi);
   return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// The same for FP16: every finite E4M3FN value (at most 448 in magnitude,
+// at least 2^-9 when not zero) is also an FP16 value, so this is exact too.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+  f16x2_t r = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ f16x8_t e4m3x8_to_f16x8(uint32_t lo, uint32_t hi) {
+  u32x4_t v;
+  v[0] = e4m3x2_to_f16x2<false>(lo);
+  v[1] = e4m3x2_to_f16x2<true>(lo);
+  v[2] = e4m3x2_to_f16x2<false>(hi);
+  v[3] = e4m3x2_to_f16x2<true>(hi);
+  return __builtin_bit_cast(f16x8_t, v);
 }
 
 // Streaming 16-byte accesses (non-temporal: data used once, keep it out of

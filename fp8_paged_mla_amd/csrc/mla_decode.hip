@@ -25,12 +25,12 @@
 //    MFMA 16x16x32 bf16 (M = 16 tokens, N = 16 heads, K = 576 in 18 steps),
 //    K read from LDS and converted FP8 -> bf16 right before the MFMA, q held
 //    in registers for as long as the request lasts;
-//  * the softmax is exchanged through LDS (wave maxima, then bf16
+//  * the softmax is exchanged through LDS (wave maxima, then FP16
 //    probabilities) so that all waves share one running maximum per head;
 //  * wave w owns output columns [64w, 64w+64) of O^T = V^T P^T (MFMA
-//    16x16x32 bf16, M = 16 columns, N = 16 heads, K = 32 tokens), reading the
-//    transposed FP8 value operand with ds_read_b64_tr_b8: no cross-wave
-//    reduction of O.
+//    16x16x32 f16, M = 16 columns, N = 16 heads, K = 32 tokens), reading the
+//    transposed FP8 value operand with ds_read_b64_tr_b8 and converting it
+//    to FP16 (exact): no cross-wave reduction of O.
 // KV bytes move from HBM once per head group; each value byte is converted
 // once per wave that consumes it.
 #include "decode_host.h"
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       for (int c = 0; c < 4; ++c)
         *reinterpret_cast<uint2*>(op + 16 * c) =
             make_uint2(pack_f16x2(O[c][0] * inv, O[c][1] * inv), pack_f16x2(O[c][2] * inv, O[c][3] * inv));
-      if (w == 0 && g == 0) p.part_lse[piece] = m_run + __builtin_amdgcn_logf(l);
+      if (w == 0 && g == 0) p.part_lse[piece] = m_run + __builtin_amdgcn_logf(l) - kPScaleLog2;
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -341,12 +341,12 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     }
     m_run = m_new;
     float pr[4];
+    const float m_p = m_new - kPScaleLog2;  // probabilities scaled by 2^15 (FP16 P.V)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
-    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]);
-    const uint32_t p23 = pack_bf16x2(pr[2], pr[3]);
-    l_w += (bf16_bits_to_f32(p01 & 0xFFFFu) + bf16_bits_to_f32(p01 >> 16)) +
-           (bf16_bits_to_f32(p23 & 0xFFFFu) + bf16_bits_to_f32(p23 >> 16));
+    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r] - m_p);
+    const uint32_t p01 = pack_f16x2(pr[0], pr[1]);
+    const uint32_t p23 = pack_f16x2(pr[2], pr[3]);
+    l_w += (f16_lo(p01) + f16_hi(p01)) + (f16_lo(p23) + f16_hi(p23));
     p_lds[w][lane] = make_uint2(p01, p23);
     // rows of tile k+1 (and a new query) landed; younger: index of k+3 unless
     // a query was copied after it, and rows of k+2 if issued
@@ -358,13 +358,13 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       if (w < 2 && k + 2 < ntiles) issue_tile(k + 2, ix_cur);
     }
 
-    bf16x8_t pb[4];
+    f16x8_t pb[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const uint2 x = p_lds[2 * st][lane];
       const uint2 y = p_lds[2 * st + 1][lane];
       u32x4_t v = {x.x, x.y, y.x, y.y};
-      pb[st] = __builtin_bit_cast(bf16x8_t, v);
+      pb[st] = __builtin_bit_cast(f16x8_t, v);
     }
     // Rows past the request's end in a partial tile are copies of the tile's
     // first row with probability 0, so their value bytes need no masking.
@@ -372,8 +372,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            e4m3x8_to_bf16x8((uint32_t)vt[st][c].x, (uint32_t)vt[st][c].y), pb[st], O[c], 0, 0, 0);
+        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            e4m3x8_to_f16x8((uint32_t)vt[st][c].x, (uint32_t)vt[st][c].y), pb[st], O[c], 0, 0, 0);
 
     if (last_of_request || k + 1 == ntiles) finish_request(whole_request && last_of_request);
     if (new_q) {

@@ -14,8 +14,9 @@
 //  * the two waves of a head group exchange maxima and probabilities
 //    through LDS;
 //  * for P.V, wave w owns output columns [256(w >> 2), +256) of its head
-//    group: O^T = V^T P^T over all 64 tokens (16 column blocks of 16), with
-//    the transposed FP8 value operand read by ds_read_b64_tr_b8.
+//    group: O^T = V^T P^T over all 64 tokens (16 column blocks of 16, MFMA
+//    16x16x32 f16 on FP16 probabilities), with the transposed FP8 value
+//    operand read by ds_read_b64_tr_b8.
 // Rows are copied global -> LDS (global_load_lds) into three slots of 64
 // rows: tile k+2 goes into the slot of tile k-1 once every wave has finished
 // tile k-1's value reads (the first barrier of tile k), ~1.5 tiles ahead.
@@ -272,7 +273,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       for (int c = 0; c < VBLOCKS; ++c)
         *reinterpret_cast<uint2*>(op + 16 * c) =
             make_uint2(pack_f16x2(O[c][0] * inv, O[c][1] * inv), pack_f16x2(O[c][2] * inv, O[c][3] * inv));
-      if (half == 0 && g == 0) p.part_lse[piece] = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l);
+      if (half == 0 && g == 0)
+        p.part_lse[piece] = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l) - kPScaleLog2;
     }
 #pragma unroll
     for (int c = 0; c < VBLOCKS; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -350,17 +352,16 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     }
     m_run = m_new;
     float pr0[4], pr1[4];
+    const float m_p = m_sub - kPScaleLog2;  // probabilities scaled by 2^15 (FP16 P.V)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      pr0[r] = __builtin_amdgcn_exp2f(s0[r] - m_sub);
-      pr1[r] = __builtin_amdgcn_exp2f(s1[r] - m_sub);
+      pr0[r] = __builtin_amdgcn_exp2f(s0[r] - m_p);
+      pr1[r] = __builtin_amdgcn_exp2f(s1[r] - m_p);
     }
-    const uint32_t p01 = pack_bf16x2(pr0[0], pr0[1]), p23 = pack_bf16x2(pr0[2], pr0[3]);
-    const uint32_t q01 = pack_bf16x2(pr1[0], pr1[1]), q23 = pack_bf16x2(pr1[2], pr1[3]);
-    l_w += (bf16_bits_to_f32(p01 & 0xFFFFu) + bf16_bits_to_f32(p01 >> 16)) +
-           (bf16_bits_to_f32(p23 & 0xFFFFu) + bf16_bits_to_f32(p23 >> 16)) +
-           (bf16_bits_to_f32(q01 & 0xFFFFu) + bf16_bits_to_f32(q01 >> 16)) +
-           (bf16_bits_to_f32(q23 & 0xFFFFu) + bf16_bits_to_f32(q23 >> 16));
+    const uint32_t p01 = pack_f16x2(pr0[0], pr0[1]), p23 = pack_f16x2(pr0[2], pr0[3]);
+    const uint32_t q01 = pack_f16x2(pr1[0], pr1[1]), q23 = pack_f16x2(pr1[2], pr1[3]);
+    l_w += (f16_lo(p01) + f16_hi(p01)) + (f16_lo(p23) + f16_hi(p23)) +
+           (f16_lo(q01) + f16_hi(q01)) + (f16_lo(q23) + f16_hi(q23));
     p_lds[w][0][lane] = make_uint2(p01, p23);
     p_lds[w][1][lane] = make_uint2(q01, q23);
     // rows of tile k+1 landed (younger: index k+3, maybe a query, rows k+2)
@@ -374,14 +375,14 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       const uint2 x = p_lds[hgl + 4 * st][0][lane];
       const uint2 y = p_lds[hgl + 4 * st][1][lane];
       const u32x4_t pv = {x.x, x.y, y.x, y.y};
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+      const f16x8_t pb = __builtin_bit_cast(f16x8_t, pv);
       const uint8_t* vb = slot + tr_off + 32 * ROWB * st;
 #pragma unroll
       for (int c = 0; c < VBLOCKS; ++c) {
         const i32x2_t vt = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) i32x2_t*)(vb + 16 * c));
-        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8((uint32_t)vt.x, (uint32_t)vt.y),
-                                                       pb, O[c], 0, 0, 0);
+        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16x8((uint32_t)vt.x, (uint32_t)vt.y),
+                                                      pb, O[c], 0, 0, 0);
       }
     }
 
