@@ -157,7 +157,8 @@ int scatter_cast_bf16_fp8(const uint16_t* src, int64_t n, int64_t src_row_stride
  * Each request's tokens are cut into 128-token tiles; the list of all tiles
  * is split into equal segments over the compute units (flash-decoding
  * split-K), and a second kernel merges the pieces of requests that span
- * several segments.  The host never reads kv_indptr, so the call stays
+ * several segments.  With 64 or more heads and at least 4 64-token tiles per
+ * workgroup slot, 64-head workgroups walk 64-token tiles instead.  The host never reads kv_indptr, so the call stays
  * asynchronous.
  */
 int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,

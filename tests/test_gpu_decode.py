@@ -150,8 +150,10 @@ def test_deterministic(dev):
 
 def test_workspace_reuse_across_shapes(dev):
     # One workspace, filled with garbage first, reused by calls of different
-    # shapes: the workspace is pure scratch, every call must match the oracle.
-    shapes = [(3, 32, [3000, 50, 9000]), (5, 16, [700, 1, 0, 2049, 130]), (2, 17, [4000, 4000])]
+    # shapes (split requests, head groups): the workspace is pure scratch,
+    # every call must match the oracle.
+    shapes = [(3, 32, [3000, 50, 9000]), (5, 16, [700, 1, 0, 2049, 130]), (2, 17, [4000, 4000]),
+              (40, 16, [1500 + 37 * i for i in range(40)])]
     need = max(fm.mla_decode_fp8_workspace_bytes(len(L), H, sum(L), dev) for _, H, L in shapes)
     ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=dev)
     for rep in range(2):
@@ -162,6 +164,28 @@ def test_workspace_reuse_across_shapes(dev):
             torch.cuda.synchronize()
             ref = oracle.mla_decode_ref(*oracle_args(w))
             assert_attention_close(out, ref, "reuse %d/%d" % (rep, i))
+
+
+def test_workspace_shared_with_other_entry_points(dev):
+    # One garbage-filled workspace shared by the FP8 decode, the BF16 decode
+    # and the extend path (one query token per request, which is decode),
+    # called in turn twice: each call overwrites what the others left.
+    w = workloads.small(6, 16, [2100, 900, 4000, 64, 3000, 1200], seed=31, device=dev)
+    need = max(fm.mla_decode_fp8_workspace_bytes(w.B, w.H, w.total_tokens, dev),
+               fm.mla_decode_bf16_workspace_bytes(w.B, w.H, w.total_tokens, dev),
+               fm.mla_extend_fp8_workspace_bytes(w.B, w.H, w.B, dev))
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=dev)
+    ref = oracle.mla_decode_ref(*oracle_args(w))
+    rows16 = fm.cast_pool_fp8_bf16(w.pool)
+    qo = torch.arange(w.B + 1, dtype=torch.int32, device=dev)
+    for rep in range(2):
+        a = fm.mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale, workspace=ws)
+        b = fm.mla_decode_bf16(w.q, rows16, w.indptr, w.indices, w.scale, w.sm_scale, workspace=ws)
+        c = fm.mla_extend_fp8(w.q.reshape(w.B, w.H, -1), w.pool, qo, w.indptr, w.indices, w.scale,
+                              w.sm_scale, causal=False, workspace=ws)
+        torch.cuda.synchronize()
+        for name, out in (("fp8", a), ("bf16", b), ("extend", c)):
+            assert_attention_close(out, ref, "shared workspace %s %d" % (name, rep))
 
 
 def test_slot_relocation_invariance(dev):
