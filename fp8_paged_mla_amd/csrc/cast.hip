@@ -221,7 +221,7 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_cast_kernel(
       const uint32_t s = (uint32_t)id_ring[w][id_slot][r];  // negative ids compare as large
       const uint8_t* src = pool + (uint64_t)(s < max_slot ? s : max_slot) * KV_WIDTH +
                            16 * (P - KV_CHUNKS * r);
-      decode::issue_lds_dma16(src, __builtin_amdgcn_readfirstlane(
+      decode::issue_lds_dma16_nt(src, __builtin_amdgcn_readfirstlane(
                                        rows_base + GATHER_OPS * 1024 * slot + 1024 * j));
     }
   };
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_cast_kernel(
     }
     u32x4_t* dst = out + (gw + k * nw) * GATHER_ROWS * (KV_WIDTH / 8) + lane;
 #pragma unroll
-    for (int h = 0; h < GATHER_STORES; ++h) store16_nt(dst + 64 * h, convert8(v[h]));
+    for (int h = 0; h < GATHER_STORES; ++h) store16_dev(dst + 64 * h, convert8(v[h]));
   }
   decode::wait_vm<0>();
   // rows past the last whole chunk, 8 bytes per lane
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_cast_kernel(
     const int64_t r = e / (KV_WIDTH / 8);
     const int c = (int)(e - r * (KV_WIDTH / 8));
     const uint32_t s = (uint32_t)indices[r];
-    store16_nt(&out[e], convert8(load8_nt(pool + (uint64_t)(s < max_slot ? s : max_slot) * KV_WIDTH + 8 * c)));
+    store16_dev(&out[e], convert8(load8_nt(pool + (uint64_t)(s < max_slot ? s : max_slot) * KV_WIDTH + 8 * c)));
   }
 }
 

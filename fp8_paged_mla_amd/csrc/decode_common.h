@@ -297,6 +297,17 @@ __device__ __forceinline__ void issue_lds_dma16(const void* g, uint32_t lds_base
                : "memory", "m0");
 }
 
+// The same for bytes read once (non-temporal hint: their lines are not kept
+// for reuse).  Measured on MI355X: the gather-cast's rows 7% and the 16-head
+// decode's rows (one head group per segment) 1% faster than with the default
+// policy; the full-pool cast's input 1% slower.
+__device__ __forceinline__ void issue_lds_dma16_nt(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N));

@@ -67,6 +67,13 @@ __device__ __forceinline__ u32x2_t load8_nt(const void* p) {
 __device__ __forceinline__ void store16_nt(void* p, u32x4_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
 }
+// 16-byte store at device scope (sc1): written through to the device's
+// coherence point instead of being kept in the XCD's L2.  The gather-cast's
+// 18 KB row-block writes run 11% faster this way on MI355X, the full-pool
+// cast's streaming writes 8% slower (they keep store16_nt).
+__device__ __forceinline__ void store16_dev(void* p, u32x4_t v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
 
 // Per byte of w: 0x80 where the byte is an E4M3FN NaN (low 7 bits all ones).
 __device__ __forceinline__ uint32_t e4m3_nan_flags(uint32_t w) {

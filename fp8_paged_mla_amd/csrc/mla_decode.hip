@@ -70,6 +70,10 @@ __device__ __forceinline__ void wait_vm_upto(int n) {
 // rows fall in distinct banks.
 __device__ __forceinline__ int tile_row(int w, int m) { return 16 * w + ((w & 1) ? (m ^ 12) : m); }
 
+// NT_ROWS: copy rows with the non-temporal hint (one head group per
+// segment: nothing re-reads them); with several head groups the segment's
+// workgroups share its rows through L2 and keep the default policy.
+template <bool NT_ROWS>
 __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p) {
   // Two row tiles (the one being computed and the next one landing) and the
   // softmax exchange.
@@ -139,7 +143,10 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
       const uint32_t s = (uint32_t)__shfl(idx, r & 15);
       const uint8_t* a = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
-      if (j < DMA_OPS - 1 || P < 16 * ROW_SLOTS) issue_lds_dma16(a, base + 1024 * j);
+      if (j < DMA_OPS - 1 || P < 16 * ROW_SLOTS) {
+        if constexpr (NT_ROWS) issue_lds_dma16_nt(a, base + 1024 * j);
+        else issue_lds_dma16(a, base + 1024 * j);
+      }
     }
   };
 
@@ -517,7 +524,10 @@ hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t 
   const decode::SplitParams sp = make_split_params(q, kv_pool, num_slots, kv_indptr, kv_indices,
                                                    total_tokens, batch, num_heads, scale,
                                                    sm_scale, out, workspace, pl);
-  hipLaunchKernelGGL(mla_split_kernel, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
+  if (pl.HG == 1)
+    hipLaunchKernelGGL(mla_split_kernel<true>, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
+  else
+    hipLaunchKernelGGL(mla_split_kernel<false>, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || total_tokens == 0) return e;  // no tokens: nothing to merge
   return launch_mla_combine(sp, stream);
