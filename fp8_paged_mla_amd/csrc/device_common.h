@@ -74,6 +74,12 @@ __device__ __forceinline__ void store16_nt(void* p, u32x4_t v) {
 __device__ __forceinline__ void store16_dev(void* p, u32x4_t v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
 }
+// 8-byte store at device scope; the write path's scattered 576-byte rows
+// measured 2% faster this way than with the default policy (non-temporal
+// stores: 13% slower).
+__device__ __forceinline__ void store8_dev(void* p, u32x2_t v) {
+  asm volatile("global_store_dwordx2 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
 
 // Per byte of w: 0x80 where the byte is an E4M3FN NaN (low 7 bits all ones).
 __device__ __forceinline__ uint32_t e4m3_nan_flags(uint32_t w) {

@@ -180,7 +180,13 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
       const uint32_t s = (uint32_t)__shfl(idx, r & 7);
       const uint8_t* a = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
-      if (j < DMA_OPS - 1 || P < ROWS_PER_WAVE * ROW_SLOTS) issue_lds_dma16(a, base + 1024 * j);
+      if (j < DMA_OPS - 1 || P < ROWS_PER_WAVE * ROW_SLOTS) {
+        // decode reads each row once per head group, close together in time
+        // (non-temporal hint); extend re-reads a request's rows for each of
+        // its query blocks (default policy)
+        if constexpr (!EXT) issue_lds_dma16_nt(a, base + 1024 * j);
+        else issue_lds_dma16(a, base + 1024 * j);
+      }
     }
   };
 

@@ -101,8 +101,7 @@ __global__ __launch_bounds__(SC_THREADS) void scatter_cast_kernel(
   for (int u = 0; u < SC_UNROLL; ++u) {
     const int64_t r = r0 + u * SC_ROWS_PER_PASS;
     if (r < n && slot[u] < num_slots)
-      *reinterpret_cast<u32x2_t*>(pool + (uint64_t)slot[u] * KV_WIDTH + 8 * c) =
-          encode8<SATURATE>(v[u], inv_scale);
+      store8_dev(pool + (uint64_t)slot[u] * KV_WIDTH + 8 * c, encode8<SATURATE>(v[u], inv_scale));
   }
 }
 
