@@ -37,6 +37,37 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 constexpr int64_t kMaxSlots = (int64_t)UINT32_MAX;  // slot ids are 32-bit
 constexpr int64_t kMaxTokens = (int64_t)INT32_MAX;  // kv_indptr is int32
 
+// Checks shared by the decode entry points (everything but the workspace).
+int check_decode_fp8_args(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                          const int32_t* kv_indptr, const int32_t* kv_indices,
+                          int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
+                          float sm_scale, const uint16_t* out) {
+  if (batch < 1 || batch > FP8MLA_MAX_BATCH || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS ||
+      total_tokens < 0 || total_tokens > kMaxTokens || num_slots < 0 || num_slots > kMaxSlots)
+    return FP8MLA_ERR_BAD_SHAPE;
+  if (total_tokens > 0 && num_slots == 0) return FP8MLA_ERR_BAD_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.0f) || !isfinite(sm_scale)) return FP8MLA_ERR_BAD_SCALAR;
+  if (!q || !kv_indptr || !out) return FP8MLA_ERR_NULL_PTR;
+  if (total_tokens > 0 && (!kv_pool || !kv_indices)) return FP8MLA_ERR_NULL_PTR;
+  if (!aligned16(q) || !aligned16(out) || !aligned4(kv_indptr)) return FP8MLA_ERR_MISALIGNED;
+  if (total_tokens > 0 && (!aligned16(kv_pool) || !aligned4(kv_indices)))
+    return FP8MLA_ERR_MISALIGNED;
+  return FP8MLA_OK;
+}
+
+// Sizes an extend call accepts: every count in range, the virtual requests
+// and the tile bound of their CSR within what the kernels address.
+bool extend_sizes_ok(int32_t batch, int32_t num_heads, int64_t total_q, int64_t total_kv) {
+  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_q < 0 ||
+      total_q >= fp8mla::kExtendMaxQueryRows || total_kv < 0 || total_kv > kMaxTokens)
+    return false;
+  if (total_q * num_heads > (int64_t)INT32_MAX) return false;  // query rows
+  const int rows = (num_heads + 15) / 16 * 16;
+  const int64_t T = rows <= 64 ? 64 / rows : 1;
+  if ((int64_t)batch + (total_q + T - 1) / T > fp8mla::kExtendMaxVirtual) return false;
+  return fp8mla::extend_tile_bound(batch, num_heads, total_q, total_kv) <= fp8mla::kExtendMaxTiles;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,10 +137,7 @@ int scatter_cast_bf16_fp8(const uint16_t* src, int64_t n, int64_t src_row_stride
 }
 
 size_t mla_extend_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_q) {
-  if (batch < 1 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS || total_q < 0 ||
-      total_q >= fp8mla::kExtendMaxQueryRows || batch > INT32_MAX / 2)
-    return 0;
-  if (total_q == 0) return 0;
+  if (!extend_sizes_ok(batch, num_heads, total_q, 0) || total_q == 0) return 0;
   const int cus = current_device_cus();
   if (cus <= 0) return 0;
   return fp8mla::plan_mla_extend(batch, num_heads, total_q, cus).workspace_bytes;
@@ -120,12 +148,10 @@ int mla_extend_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
                    int64_t total_q, int64_t total_kv, int32_t batch, int32_t num_heads,
                    float scale, float sm_scale, int32_t causal, uint16_t* out, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  if (batch < 1 || batch > INT32_MAX / 2 || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS ||
-      total_q < 0 || total_q >= fp8mla::kExtendMaxQueryRows || total_kv < 0 ||
-      total_kv > kMaxTokens || num_slots < 0 || num_slots > kMaxSlots)
+  if (!extend_sizes_ok(batch, num_heads, total_q, total_kv) || num_slots < 0 ||
+      num_slots > kMaxSlots)
     return FP8MLA_ERR_BAD_SHAPE;
   if (total_kv > 0 && num_slots == 0) return FP8MLA_ERR_BAD_SHAPE;
-  if (total_q * num_heads > (int64_t)INT32_MAX) return FP8MLA_ERR_BAD_SHAPE;  // query rows
   if (!isfinite(scale) || !(scale > 0.0f) || !isfinite(sm_scale)) return FP8MLA_ERR_BAD_SCALAR;
   if (total_q == 0) return FP8MLA_OK;
   if (!q || !qo_indptr || !kv_indptr || !out || !workspace) return FP8MLA_ERR_NULL_PTR;
@@ -161,16 +187,11 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
                    const int32_t* kv_indptr, const int32_t* kv_indices, int64_t total_tokens,
                    int32_t batch, int32_t num_heads, float scale, float sm_scale, uint16_t* out,
                    void* workspace, size_t workspace_bytes, void* stream) {
-  if (batch < 1 || batch > FP8MLA_MAX_BATCH || num_heads < 1 || num_heads > FP8MLA_MAX_HEADS ||
-      total_tokens < 0 || total_tokens > kMaxTokens || num_slots < 0 || num_slots > kMaxSlots)
-    return FP8MLA_ERR_BAD_SHAPE;
-  if (total_tokens > 0 && num_slots == 0) return FP8MLA_ERR_BAD_SHAPE;
-  if (!isfinite(scale) || !(scale > 0.0f) || !isfinite(sm_scale)) return FP8MLA_ERR_BAD_SCALAR;
-  if (!q || !kv_indptr || !out) return FP8MLA_ERR_NULL_PTR;
-  if (total_tokens > 0 && (!kv_pool || !kv_indices || !workspace)) return FP8MLA_ERR_NULL_PTR;
-  if (!aligned16(q) || !aligned16(out) || !aligned4(kv_indptr)) return FP8MLA_ERR_MISALIGNED;
-  if (total_tokens > 0 && (!aligned16(kv_pool) || !aligned4(kv_indices) || !aligned16(workspace)))
-    return FP8MLA_ERR_MISALIGNED;
+  const int st = check_decode_fp8_args(q, kv_pool, num_slots, kv_indptr, kv_indices, total_tokens,
+                                       batch, num_heads, scale, sm_scale, out);
+  if (st != FP8MLA_OK) return st;
+  if (total_tokens > 0 && !workspace) return FP8MLA_ERR_NULL_PTR;
+  if (total_tokens > 0 && !aligned16(workspace)) return FP8MLA_ERR_MISALIGNED;
   const int cus = current_device_cus();
   if (cus <= 0) return FP8MLA_ERR_HIP;
   const fp8mla::DecodePlan plan = fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus,

@@ -22,7 +22,7 @@ struct SplitParams {
   uint16_t* out;
   uint16_t* part_o;         // fp16 bits
   float* part_lse;
-  int2* req_pieces;         // per request: (segment of its first piece, number of pieces)
+  int2* req_pieces;         // per request: (slot of its first piece, number of pieces)
   uint32_t max_slot;
   int32_t total_tokens;
   int32_t B;
@@ -36,10 +36,10 @@ struct SplitParams {
   float kv_scale;
   // Extend (several query tokens per request) only.  The kernels then walk
   // virtual requests, one per (request, block of query tokens), built on the
-  // device: indptr is their CSR of visible-token counts (padded with empty
-  // requests up to B), and per virtual request vinfo holds (offset from a CSR
-  // position to its kv_indices entry, first query row | (tokens in the block
-  // - 1) << 29).
+  // device: indptr is their CSR of tile counts (64-token tiles of the tokens
+  // each one sees, padded with empty requests up to B), and per virtual
+  // request vinfo holds (its first kv_indices entry, first query row |
+  // (tokens in the block - 1) << 23 | (tokens in its last tile - 1) << 25).
   const int2* vinfo;
   int32_t rows_per_tok;  // query rows per token (heads rounded up to 16) if <= 64, else 0
   int32_t causal;
@@ -54,8 +54,12 @@ struct SplitParams {
 // scale cancels in O / l and is taken out of the log-sum-exp of a partial.
 constexpr float kPScaleLog2 = 15.0f;
 
-constexpr int kExtQ0Bits = 29;                 // first query row in the low 29 bits of vinfo.y
+// Fields of vinfo.y (extend): first query row (23 bits), tokens in the block
+// - 1 (2 bits), tokens in the last tile - 1 (6 bits).
+constexpr int kExtQ0Bits = 23;
 constexpr int kExtQ0Mask = (1 << kExtQ0Bits) - 1;
+constexpr int kExtTokShift = 23;
+constexpr int kExtTailShift = 25;
 
 __device__ __forceinline__ float wave_max_over_groups(float x) {
   // lanes h, h+16, h+32, h+48 hold the same head
@@ -110,7 +114,9 @@ __device__ __forceinline__ int request_tiles(const int32_t* indptr, int b, int B
 // most W / (TILE_W + START_W) segments every segment holds a tile and the
 // pieces of a request are consecutive segments.  (Weights fit in int: with
 // tiles of at least 64 tokens W <= 4 (N / 64 + B) + 2 B < 2^31 for
-// N < 2^31 and B <= 2^24, the batch limit the host enforces.)
+// N < 2^31 and B <= 2^24, the batch limit the host enforces; for extend,
+// whose CSR counts tiles (SHIFT 0), W <= 4 N + 6 B with N <= 2^28 tiles and
+// B <= 2^25 virtual requests, the bounds its host checks.)
 struct SegmentSpan {
   int nseg;    // segments in use
   int W;       // total weight
@@ -198,19 +204,20 @@ __device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int 
 }
 
 // Walks the tiles of consecutive requests: request b, tile j of its nt
-// tiles, request range [lo, hi).  Requests without tokens are skipped.  The
-// kv_indptr values come from a 64-entry window held one entry per lane.
-// With EXT the requests are virtual (see SplitParams) and the cursor also
-// carries the current one's index offset and query rows (from a window of
-// vinfo held the same way).
+// tiles, kv_indices range [lo, hi).  Requests without tokens are skipped.
+// The kv_indptr values come from a 64-entry window held one entry per lane.
+// With EXT the requests are virtual (see SplitParams): the window holds
+// their tile CSR, and the cursor takes lo, hi and the query rows from a
+// window of vinfo held the same way.
 template <bool EXT>
 struct CursorExtFields {};  // decode: no extra fields (the cursor must stay in registers)
 template <>
 struct CursorExtFields<true> {
-  int delta, q0n;            // vinfo of the current virtual request
-  int win_delta, win_q0n;    // vinfo window, one entry per lane
+  int q0n;                   // vinfo.y of the current virtual request
+  int win_kv0, win_q0n;      // vinfo window, one entry per lane
   __device__ __forceinline__ int q_row0() const { return q0n & kExtQ0Mask; }
-  __device__ __forceinline__ int q_tokens() const { return (q0n >> kExtQ0Bits) + 1; }
+  __device__ __forceinline__ int q_tokens() const { return ((q0n >> kExtTokShift) & 3) + 1; }
+  __device__ __forceinline__ int tail() const { return ((q0n >> kExtTailShift) & 63) + 1; }
 };
 
 template <int SHIFT, bool EXT = false>
@@ -225,7 +232,7 @@ struct TileCursor : CursorExtFields<EXT> {
     win_val = clamp_tok(p.indptr[min(first + lane, p.B)], p.total_tokens);
     if constexpr (EXT) {
       const int2 vi = p.vinfo[min(first + lane, p.B - 1)];
-      this->win_delta = vi.x;
+      this->win_kv0 = vi.x;
       this->win_q0n = vi.y;
     }
   }
@@ -237,12 +244,15 @@ struct TileCursor : CursorExtFields<EXT> {
     const int l = __builtin_amdgcn_readlane(win_val, valid ? nb - win : 0);
     const int h = max(l, __builtin_amdgcn_readlane(win_val, valid ? nb + 1 - win : 0));
     b = nb;
-    lo = valid ? l : 0;
-    hi = valid ? h : 0;
-    nt = valid ? (h - l + (1 << SHIFT) - 1) >> SHIFT : 0;
     if constexpr (EXT) {
-      this->delta = valid ? __builtin_amdgcn_readlane(this->win_delta, nb - win) : 0;
       this->q0n = valid ? __builtin_amdgcn_readlane(this->win_q0n, nb - win) : 0;
+      nt = valid ? h - l : 0;
+      lo = valid ? __builtin_amdgcn_readlane(this->win_kv0, nb - win) : 0;
+      hi = nt > 0 ? lo + ((nt - 1) << SHIFT) + this->tail() : lo;
+    } else {
+      lo = valid ? l : 0;
+      hi = valid ? h : 0;
+      nt = valid ? (h - l + (1 << SHIFT) - 1) >> SHIFT : 0;
     }
   }
   __device__ __forceinline__ void start(const SplitParams& p, int b0, int j0, int lane) {
@@ -315,7 +325,24 @@ __device__ __forceinline__ void wait_vm() {
 
 __device__ __forceinline__ void pin(int32_t& x) { asm volatile("" : "+v"(x)); }
 
-// ---- partial results.  Partial outputs are stored as fp16 (round to
+// ---- partial results.  A segment writes at most two partial pieces: one for
+// its first request (begun in an earlier segment, or continuing past this
+// one when it is the segment's only request) and one for its last request
+// (continuing past the segment); every other request of the segment lies
+// inside it and gets its final output directly.  The partial area therefore
+// holds 2 * nseg pieces of Hp rows whatever the batch: slot 2s for the first
+// request of segment s, slot 2s + 1 for its last.  A request whose tiles
+// span segments s0 .. s0 + np - 1 has its pieces in slot `first` = 2 s0 +
+// (0 if it is the first request of s0, else 1), then in slot 2s of every
+// later segment s, where it is necessarily the first request.
+__device__ __forceinline__ int piece_slot(int seg, bool first_of_segment) {
+  return 2 * seg + (first_of_segment ? 0 : 1);
+}
+__device__ __forceinline__ int nth_piece(int first, int i) {
+  return i == 0 ? first : (first & ~1) + 2 * i;
+}
+
+// Partial outputs are stored as fp16 (round to
 // nearest even) before the per-tensor scale; the rows this library is fed
 // hold E4M3 values (|v| <= 448), so the partials, convex combinations of
 // them, cannot overflow, and fp16's 11-bit significand is finer than the
@@ -327,27 +354,27 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 __device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w).x; }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w).y; }
 
-// Merge of the np partial results (pieces s0 + b .. s0 + np - 1 + b) of
-// request b for one head, by one wave: out = scale * sum_s w_s o_s / sum_s
+// Merge of the np partial results of a request for one head, by one wave
+// (pieces nth_piece(first, i), i < np): out = scale * sum_s w_s o_s / sum_s
 // w_s with w_s = 2^(lse_s - max lse).  Pieces are taken eight at a time with
 // all their loads issued together (one memory latency per eight pieces) and
 // folded in with a running maximum.  Lane l produces output columns
 // 8l .. 8l+7.
 __device__ __forceinline__ void merge_pieces(const uint16_t* part_o, const float* part_lse, int Hp,
-                                             int b, int s0, int np, int head, float kv_scale,
+                                             int first, int np, int head, float kv_scale,
                                              uint16_t* op, int lane) {
-  const float* lse = part_lse + (int64_t)(s0 + b) * Hp + head;  // piece i at lse[i * Hp]
-  const uint16_t* po = part_o + ((int64_t)(s0 + b) * Hp + head) * V_WIDTH + 8 * lane;
-  const int64_t pstride = (int64_t)Hp * V_WIDTH;  // elements between consecutive pieces
+  const float* lse = part_lse + head;  // piece s at lse[s * Hp]
+  const uint16_t* po = part_o + (int64_t)head * V_WIDTH + 8 * lane;
+  const int64_t pstride = (int64_t)Hp * V_WIDTH;  // elements between consecutive piece slots
   float M = -INFINITY, den = 0.f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < np; base += 8) {
     const int cnt = min(8, np - base);
-    const float lv = lane < cnt ? lse[(int64_t)(base + lane) * Hp] : -INFINITY;
+    const float lv = lane < cnt ? lse[(int64_t)nth_piece(first, base + lane) * Hp] : -INFINITY;
     uint4 x[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)  // u >= cnt re-reads the last piece (in bounds, unused)
-      x[u] = *reinterpret_cast<const uint4*>(po + (int64_t)(base + min(u, cnt - 1)) * pstride);
+      x[u] = *reinterpret_cast<const uint4*>(po + (int64_t)nth_piece(first, base + min(u, cnt - 1)) * pstride);
     float cm = lv;
 #pragma unroll
     for (int off = 1; off < 8; off <<= 1) cm = fmaxf(cm, __shfl_xor(cm, off));

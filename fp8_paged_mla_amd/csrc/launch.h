@@ -94,16 +94,30 @@ struct ExtendPlan {
   int32_t xcd_per;
   int32_t grid;
   size_t vstart_offset;   // int32 [batch + 1]: first virtual request of each request
-  size_t vindptr_offset;  // int32 [vmax + 1]: CSR of visible-token counts
+  size_t vindptr_offset;  // int32 [vmax + 1]: CSR of the tiles each virtual request reads
   size_t vinfo_offset;    // int2 [vmax]
   size_t pieces_offset;   // int2 [vmax]: (segment of the first piece, pieces)
-  size_t part_o_offset;   // fp16 [(nseg + vmax) * Hp * 512]
-  size_t lse_offset;      // float [(nseg + vmax) * Hp]
+  size_t part_o_offset;   // fp16 [2 * nseg * Hp * 512]: two piece slots per segment
+  size_t lse_offset;      // float [2 * nseg * Hp]
   size_t workspace_bytes; // also holds the header {virtual requests, CSR total} at offset 0
 };
 
-constexpr int64_t kExtendMaxQueryRows = (int64_t)1 << 29;   // first query row packs into 29 bits
-constexpr int64_t kExtendMaxVirtualTokens = (int64_t)1 << 29;  // CSR total the split can address
+// Limits of an extend call.  Query rows pack into 23 bits of the virtual
+// requests' info.  The virtual requests' CSR counts 64-token tiles and must
+// stay within kExtendMaxTiles, so that the split's int32 weights (4 per
+// tile, 6 per request) cannot overflow; the host checks a bound of that
+// total computed from the sizes alone (extend_tile_bound).
+constexpr int64_t kExtendMaxQueryRows = (int64_t)1 << 23;
+constexpr int64_t kExtendMaxTiles = (int64_t)1 << 28;
+constexpr int64_t kExtendMaxVirtual = (int64_t)1 << 25;
+constexpr int kExtendTileShift = 6;  // the 64-row kernel's tile: 64 tokens
+
+// Upper bound on the tiles of the virtual requests of any extend call with
+// these sizes whose indptr arrays satisfy the contract: request b's
+// ceil(q_b / T) blocks each see at most kv_b tokens, so the tokens seen sum
+// to at most (ceil(total_q / T) + 1) * total_kv, and every block adds at
+// most one partial tile.
+int64_t extend_tile_bound(int32_t batch, int32_t num_heads, int64_t total_q, int64_t total_kv);
 
 ExtendPlan plan_mla_extend(int32_t batch, int32_t num_heads, int64_t total_q, int num_cus);
 

@@ -233,7 +233,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     if (hg == 0 && threadIdx.x == 0) {
       const int s0 = span.segment_of(P_cur + START_W);
       const int s1 = span.segment_of(P_cur + START_W + TILE_W * (cc.nt - 1));
-      p.req_pieces[cc.b] = make_int2(s0, s1 - s0 + 1);
+      p.req_pieces[cc.b] = make_int2(piece_slot(s0, cc.b == span.b0), s1 - s0 + 1);
     }
   };
   if (whole_request) record_pieces();
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
         }
       }
     } else {
-      const int64_t piece = (int64_t)(seg + cc.b) * p.Hp + head;
+      const int64_t piece = (int64_t)piece_slot(seg, cc.b == span.b0) * p.Hp + head;
       const float inv = 1.0f / l;
       uint16_t* op = p.part_o + piece * V_WIDTH + 64 * w + 4 * g;
 #pragma unroll
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const CombineParams p)
   if (head >= p.H) return;
   const int2 rp = p.req_pieces[b];
   if (rp.y <= 1) return;
-  merge_pieces(p.part_o, p.part_lse, p.Hp, b, rp.x, rp.y, head, p.kv_scale,
+  merge_pieces(p.part_o, p.part_lse, p.Hp, rp.x, rp.y, head, p.kv_scale,
                p.out + ((int64_t)b * p.H + head) * V_WIDTH, threadIdx.x & 63);
 }
 
@@ -459,12 +459,24 @@ DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_token
     pl.grid = pl.items;
   }
   // Workspace: per-request piece ranges, then partial outputs and
-  // log2-sum-exps; pieces are indexed segment + request, fewer than
-  // nseg + batch.
-  const size_t npieces = (size_t)pl.nseg + (size_t)batch;
+  // log2-sum-exps, two piece slots of Hp rows per segment.  Sized for the
+  // most piece rows any call with this batch and head count can use (all CUs
+  // in use, and either FP8 kernel where the head count admits both), so that
+  // the size does not grow with the number of tokens.
+  auto piece_rows_of = [&](DecodeKernel k) -> size_t {
+    const int wh = k == DecodeKernel::kFp8H64 ? 64 : HEADS;
+    const int64_t hg = (num_heads + wh - 1) / wh;
+    const int64_t segs = num_cus / hg > 1 ? num_cus / hg : 1;
+    return 2 * (size_t)segs * (size_t)(hg * wh);
+  };
+  size_t piece_rows = piece_rows_of(kernel);
+  if (kernel != DecodeKernel::kBf16 && num_heads >= kH64MinHeads) {
+    const size_t a = piece_rows_of(DecodeKernel::kFp8), b = piece_rows_of(DecodeKernel::kFp8H64);
+    piece_rows = a > b ? a : b;
+  }
   const size_t ranges_bytes = (size_t)batch * 2 * sizeof(int32_t);
-  const size_t o_bytes = npieces * pl.Hp * V_WIDTH * sizeof(uint16_t);
-  const size_t lse_bytes = npieces * pl.Hp * sizeof(float);
+  const size_t o_bytes = piece_rows * V_WIDTH * sizeof(uint16_t);
+  const size_t lse_bytes = piece_rows * sizeof(float);
   pl.part_o_offset = (ranges_bytes + 255) / 256 * 256;
   pl.lse_offset = pl.part_o_offset + (o_bytes + 255) / 256 * 256;
   pl.workspace_bytes = pl.lse_offset + (lse_bytes + 255) / 256 * 256;

@@ -19,10 +19,15 @@
 //    in step s), q held in registers in the same order;
 //  * the softmax is exchanged through LDS as in the FP8 kernel;
 //  * wave w owns output columns [128w, 128w + 128) of O^T = V^T P^T (MFMA
-//    16x16x32 bf16, 8 column blocks), reading the transposed value operand
-//    with ds_read_b64_tr_b16.
-// Rows must hold values within the fp16 range (|v| <= 65504) for the
-// partials; the rows produced by the casts hold E4M3 values (|v| <= 448).
+//    16x16x32 f16, 8 column blocks), reading the transposed value operand
+//    with ds_read_b64_tr_b16 and converting it to FP16; the probabilities
+//    are FP16 scaled by 2^15, as in the FP8 kernels, so that values of
+//    opposite sign up to 448 that cancel keep their rounding error inside
+//    the tolerance (BF16 probabilities, 8 significant bits, do not).
+// Rows must hold values within the fp16 range (|v| <= 65504) for the value
+// operand and the partials; BF16 values of that range convert to FP16
+// exactly down to 2^-17 in magnitude.  The rows produced by the casts hold
+// E4M3 values (|v| <= 448, exact in FP16).
 #include "decode_host.h"
 
 namespace fp8mla {
@@ -31,6 +36,13 @@ namespace {
 using namespace decode;
 
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+// Two BF16 values (low half first) to two FP16 values: exact for BF16
+// values within the FP16 range down to 2^-17 in magnitude, rounded to
+// nearest below.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return pack_f16x2(__builtin_bit_cast(float, w << 16), __builtin_bit_cast(float, w & 0xFFFF0000u));
+}
 
 constexpr int NWAVES = 4;
 constexpr int THREADS = 64 * NWAVES;             // 256
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_bf16_kernel(const SplitPara
     if (hg == 0 && threadIdx.x == 0) {
       const int s0 = span.segment_of(P_cur + START_W);
       const int s1 = span.segment_of(P_cur + START_W + TILE_W * (cc.nt - 1));
-      p.req_pieces[cc.b] = make_int2(s0, s1 - s0 + 1);
+      p.req_pieces[cc.b] = make_int2(piece_slot(s0, cc.b == span.b0), s1 - s0 + 1);
     }
   };
   if (whole_request) record_pieces();
@@ -163,14 +175,14 @@ __global__ __launch_bounds__(THREADS) void mla_split_bf16_kernel(const SplitPara
               make_uint2(pack_bf16x2(O[c][0] * inv, O[c][1] * inv), pack_bf16x2(O[c][2] * inv, O[c][3] * inv));
       }
     } else {
-      const int64_t piece = (int64_t)(seg + cc.b) * p.Hp + head;
+      const int64_t piece = (int64_t)piece_slot(seg, cc.b == span.b0) * p.Hp + head;
       const float inv = 1.0f / l;
       uint16_t* op = p.part_o + piece * V_WIDTH + 128 * w + 4 * g;
 #pragma unroll
       for (int c = 0; c < VBLOCKS; ++c)
         *reinterpret_cast<uint2*>(op + 16 * c) =
             make_uint2(pack_f16x2(O[c][0] * inv, O[c][1] * inv), pack_f16x2(O[c][2] * inv, O[c][3] * inv));
-      if (w == 0 && g == 0) p.part_lse[piece] = m_run + __builtin_amdgcn_logf(l);
+      if (w == 0 && g == 0) p.part_lse[piece] = m_run + __builtin_amdgcn_logf(l) - kPScaleLog2;
     }
 #pragma unroll
     for (int c = 0; c < VBLOCKS; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -226,12 +238,12 @@ __global__ __launch_bounds__(THREADS) void mla_split_bf16_kernel(const SplitPara
     }
     m_run = m_new;
     float pr[4];
+    const float m_p = m_new - kPScaleLog2;  // probabilities scaled by 2^15 (FP16 P.V)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sc[r] - m_new);
-    const uint32_t p01 = pack_bf16x2(pr[0], pr[1]);
-    const uint32_t p23 = pack_bf16x2(pr[2], pr[3]);
-    l_w += (bf16_bits_to_f32(p01 & 0xFFFFu) + bf16_bits_to_f32(p01 >> 16)) +
-           (bf16_bits_to_f32(p23 & 0xFFFFu) + bf16_bits_to_f32(p23 >> 16));
+    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sc[r] - m_p);
+    const uint32_t p01 = pack_f16x2(pr[0], pr[1]);
+    const uint32_t p23 = pack_f16x2(pr[2], pr[3]);
+    l_w += (f16_lo(p01) + f16_hi(p01)) + (f16_lo(p23) + f16_hi(p23));
     p_lds[w][lane] = make_uint2(p01, p23);
     __syncthreads();
 
@@ -242,16 +254,17 @@ __global__ __launch_bounds__(THREADS) void mla_split_bf16_kernel(const SplitPara
       const uint2 x = p_lds[2 * st + (g >> 1)][32 * (g & 1) + t];
       const uint2 y = p_lds[2 * st + (g >> 1)][32 * (g & 1) + 16 + t];
       const u32x4_t pv = {x.x, x.y, y.x, y.y};
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+      const f16x8_t pb = __builtin_bit_cast(f16x8_t, pv);
       const uint8_t* vb = slot + 32 * st * ROWB + tr_off + 2 * (128 * w);
 #pragma unroll
       for (int c = 0; c < VBLOCKS; ++c) {
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(vb + 32 * c));
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4_t*)(vb + 4 * ROWB + 32 * c));
-        const __attribute__((ext_vector_type(8))) short a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), pb, O[c], 0, 0, 0);
+        const i32x2_t lo = __builtin_bit_cast(i32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vb + 32 * c)));
+        const i32x2_t hi = __builtin_bit_cast(i32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(vb + 4 * ROWB + 32 * c)));
+        const u32x4_t a = {bf16x2_to_f16x2((uint32_t)lo.x), bf16x2_to_f16x2((uint32_t)lo.y),
+                           bf16x2_to_f16x2((uint32_t)hi.x), bf16x2_to_f16x2((uint32_t)hi.y)};
+        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), pb, O[c], 0, 0, 0);
       }
     }
 

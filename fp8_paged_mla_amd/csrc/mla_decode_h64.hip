@@ -51,6 +51,7 @@ constexpr int DMA_OPS = (ROWS_PER_WAVE * ROW_SLOTS + 63) / 64;  // 5
 constexpr int VBLOCKS = (V_WIDTH / 2) / 16;       // 16 output blocks per wave
 static_assert(TILE == 1 << TILE_SHIFT, "tile size");
 static_assert(TILE == kH64TileTokens, "host and kernel tile sizes agree");
+static_assert(TILE_SHIFT == kExtendTileShift, "extend's tile CSR counts this kernel's tiles");
 
 __device__ __forceinline__ void issue_load_q(bf16x8_t (&q)[QSTEPS], const uint16_t* qp) {
   // 9 pairs of 16-byte pieces 64 elements (128 bytes) apart
@@ -140,7 +141,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   }
 
   SegmentSpan span;
-  if (!find_segment<TILE_SHIFT, THREADS, WG_HEADS, !EXT>(p, seg, hs, lane, span)) return;
+  // (extend: the virtual requests' CSR counts tiles already)
+  if (!find_segment<EXT ? 0 : TILE_SHIFT, THREADS, WG_HEADS, !EXT>(p, seg, hs, lane, span)) return;
   const int ntiles = span.ntiles;
   using Cursor = TileCursor<TILE_SHIFT, EXT>;
   Cursor cc;
@@ -157,9 +159,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   auto load_next_index = [&]() -> int32_t {
     const int tlo = lc.tile_lo();
     const int tok = tlo + ROWS_PER_WAVE * w + (t & 7);
-    int off = 0;  // extend: CSR position -> kv_indices entry
-    if constexpr (EXT) off = lc.delta;
-    const int32_t* a = lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) + off : p.indices;
+    const int32_t* a = lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) : p.indices;
     const int32_t v = issue_load_i32(a);
     lc.advance(p, lane);
     return v;
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     if (hs == 0 && threadIdx.x == 0) {
       const int s0 = span.segment_of(P_cur + START_W);
       const int s1 = span.segment_of(P_cur + START_W + TILE_W * (cc.nt - 1));
-      p.req_pieces[cc.b] = make_int2(s0, s1 - s0 + 1);
+      p.req_pieces[cc.b] = make_int2(piece_slot(s0, cc.b == span.b0), s1 - s0 + 1);
     }
   };
   if (whole_request) record_pieces();
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
               make_uint2(pack_bf16x2(O[c][0] * inv, O[c][1] * inv), pack_bf16x2(O[c][2] * inv, O[c][3] * inv));
       }
     } else {
-      const int64_t piece = (int64_t)(seg + cc.b) * p.Hp + row;
+      const int64_t piece = (int64_t)piece_slot(seg, cc.b == span.b0) * p.Hp + row;
       const bool empty = EXT && l == 0.f;  // extend: no visible token in this piece
       const float inv = empty ? 0.f : 1.0f / l;
       uint16_t* op = p.part_o + piece * V_WIDTH + 256 * half + 4 * g;

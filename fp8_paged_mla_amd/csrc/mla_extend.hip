@@ -14,8 +14,9 @@
 //  1. extend_prepass_kernel (one workgroup) cuts every request's query
 //     tokens into blocks of T and lays the blocks out as virtual requests:
 //     a block reads the first n tokens of its request's list, n being its
-//     last token's limit; their CSR, and per block the offset from a CSR
-//     position to its kv_indices entry and its first query row.
+//     last token's limit; their CSR in 64-token tiles, and per block its
+//     first kv_indices entry, first query row and the tokens of its last
+//     tile.
 //  2. mla_split_h64_kernel<true> runs the 64-row split kernel over them: a
 //     block's T tokens x H heads share every KV tile, each 16-row group
 //     masked by its own token's limit.
@@ -88,14 +89,16 @@ __device__ __forceinline__ RequestRanges request_ranges(const int32_t* qo, const
 // hdr = {virtual requests V, CSR total}; vstart [B + 1]; vindptr [vmax + 1]
 // and vinfo [vmax], entries V.. padded as empty requests, so that the split
 // kernel can walk all vmax of them without reading V.  V is capped at vmax
-// (reached only by a non-monotone indptr); a CSR total past
-// kExtendMaxVirtualTokens makes every virtual request empty (nothing is
-// computed).
+// and the CSR total at kExtendMaxTiles; both caps are reached only by index
+// arrays that break the call's contract (non-monotone indptr), and then
+// every virtual request is made empty: the combine writes zero rows and no
+// read leaves its array.
 __global__ __launch_bounds__(PRE_THREADS) void extend_prepass_kernel(
     const int32_t* __restrict__ qo_indptr, const int32_t* __restrict__ kv_indptr, int32_t B,
     int32_t total_q, int32_t total_kv, int32_t T, int32_t causal, int32_t vmax,
     int32_t* __restrict__ hdr, int32_t* __restrict__ vstart, int32_t* __restrict__ vindptr,
     int2* __restrict__ vinfo) {
+  constexpr int TS = kExtendTileShift;
   // blocks per request -> first virtual request of each request
   int64_t carry = 0;
   for (int c = 0; c < B; c += PRE_THREADS) {
@@ -115,11 +118,11 @@ __global__ __launch_bounds__(PRE_THREADS) void extend_prepass_kernel(
   __syncthreads();
 
   // per virtual request: its request (the last b with vstart[b] <= v), its
-  // token block, the tokens it reads, and their CSR
+  // token block, the tokens it reads, and the CSR of their tiles
   int64_t ncarry = 0;
   for (int c = 0; c < V; c += PRE_THREADS) {
     const int v = c + (int)threadIdx.x;
-    int64_t len = 0;
+    int ntiles = 0, tail = 0;
     int kv_lo = 0, q_row = 0, ntok = 1;
     if (v < V) {
       int lo = 0, hi = B - 1;
@@ -135,20 +138,22 @@ __global__ __launch_bounds__(PRE_THREADS) void extend_prepass_kernel(
       // (the clamps only act on a non-monotone indptr: they keep every query
       // row the split kernel touches inside [0, total_q))
       ntok = min(clampi(ql - i0, 1, T), total_q);
-      len = causal ? clampi(kl - ql + i0 + ntok, 0, kl) : kl;
+      const int len = causal ? clampi(kl - ql + i0 + ntok, 0, kl) : kl;
+      ntiles = (len >> TS) + ((len & ((1 << TS) - 1)) != 0);
+      tail = len - (ntiles > 0 ? (ntiles - 1) << TS : 0);  // tokens of the last tile, 1 .. 64
       kv_lo = r.kv_lo;
       q_row = clampi(r.q_lo + i0, 0, total_q - ntok);
     }
     int64_t tot;
-    const int64_t pos = ncarry + block_exclusive_scan(len, tot);
+    const int64_t pos = ncarry + block_exclusive_scan(ntiles, tot);
     if (v < V) {
-      vindptr[v] = (int32_t)min(pos, kExtendMaxVirtualTokens);
-      vinfo[v] = make_int2(kv_lo - (int)min(pos, kExtendMaxVirtualTokens),
-                           q_row | ((ntok - 1) << kExtQ0Bits));
+      vindptr[v] = (int32_t)min(pos, kExtendMaxTiles);
+      vinfo[v] = make_int2(kv_lo, q_row | ((ntok - 1) << kExtTokShift) |
+                                      ((ntiles > 0 ? tail - 1 : 0) << kExtTailShift));
     }
     ncarry += tot;
   }
-  const bool fits = ncarry <= kExtendMaxVirtualTokens;
+  const bool fits = ncarry <= kExtendMaxTiles;
   for (int v = V + (int)threadIdx.x; v <= vmax; v += PRE_THREADS) {
     vindptr[v] = fits ? (int32_t)ncarry : 0;
     if (v < vmax) vinfo[v] = make_int2(0, 0);
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(PRE_THREADS) void extend_prepass_kernel(
     for (int v = (int)threadIdx.x; v < V; v += PRE_THREADS) vindptr[v] = 0;
   }
   if (threadIdx.x == 0) {
-    hdr[0] = fits ? V : 0;
+    hdr[0] = V;
     hdr[1] = fits ? (int32_t)ncarry : 0;
   }
 }
@@ -196,19 +201,29 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void extend_combine_kernel(const
     tk = row / p.rows_per_tok;
     head = row - tk * p.rows_per_tok;
   }
-  if (head >= p.H || tk > (vi.y >> kExtQ0Bits)) return;
+  if (head >= p.H || tk > ((vi.y >> kExtTokShift) & 3)) return;
   if (rp.y == 1) return;
   uint16_t* op = p.out + ((int64_t)((vi.y & kExtQ0Mask) + tk) * p.H + head) * V_WIDTH;
   if (rp.y == 0) {
     *reinterpret_cast<uint4*>(op + 8 * lane) = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
-  merge_pieces(p.part_o, p.part_lse, p.Hp, v, rp.x, rp.y, row, p.kv_scale, op, lane);
+  merge_pieces(p.part_o, p.part_lse, p.Hp, rp.x, rp.y, row, p.kv_scale, op, lane);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
+
+int64_t extend_tile_bound(int32_t batch, int32_t num_heads, int64_t total_q, int64_t total_kv) {
+  const int rows = (num_heads + 15) / 16 * 16;
+  const int64_t T = rows <= 64 ? 64 / rows : 1;
+  const int64_t blocks = (total_q + T - 1) / T;
+  const int64_t vmax = (int64_t)batch + blocks;
+  const int64_t tiles_of_kv = (total_kv + (1 << kExtendTileShift) - 1) >> kExtendTileShift;
+  // (blocks + 1) * tiles_of_kv cannot overflow: blocks < 2^23, tiles_of_kv < 2^25
+  return (blocks + 1) * tiles_of_kv + vmax;
+}
 
 ExtendPlan plan_mla_extend(int32_t batch, int32_t num_heads, int64_t total_q, int num_cus) {
   ExtendPlan pl{};
@@ -246,9 +261,9 @@ ExtendPlan plan_mla_extend(int32_t batch, int32_t num_heads, int64_t total_q, in
   pl.pieces_offset = off;
   off = align256(off + 8 * V);
   pl.part_o_offset = off;
-  off = align256(off + 2 * ((size_t)pl.nseg + V) * pl.Hp * V_WIDTH);
+  off = align256(off + 2 * (2 * (size_t)pl.nseg) * pl.Hp * V_WIDTH);  // two piece slots per segment
   pl.lse_offset = off;
-  off = align256(off + 4 * ((size_t)pl.nseg + V) * pl.Hp);
+  off = align256(off + 4 * (2 * (size_t)pl.nseg) * pl.Hp);
   pl.workspace_bytes = off;
   return pl;
 }
@@ -282,7 +297,7 @@ hipError_t launch_mla_extend(const uint16_t* q, const uint8_t* kv_pool, int64_t 
   sp.part_lse = reinterpret_cast<float*>(ws + pl.lse_offset);
   sp.req_pieces = pieces;
   sp.max_slot = num_slots > 0 ? (uint32_t)(num_slots - 1) : 0u;
-  sp.total_tokens = (int32_t)kExtendMaxVirtualTokens;  // bound of the CSR (clamps only)
+  sp.total_tokens = (int32_t)kExtendMaxTiles;  // bound of the tile CSR (clamps only)
   sp.B = pl.vmax;  // V real virtual requests, then empty ones
   sp.H = num_heads;
   sp.HG = pl.HG;

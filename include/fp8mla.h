@@ -169,8 +169,10 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
 /*
  * Workspace size in bytes for mla_decode_fp8 on the CURRENT device with these
  * sizes (0 when total_tokens == 0: no workspace is needed).  Returns 0 for
- * invalid sizes.  Host-only except for one query of the device's
- * compute-unit count (cached per device).
+ * invalid sizes.  For total_tokens > 0 the size depends only on batch and
+ * num_heads (8 bytes per request plus two partial results per compute unit
+ * and head), not on the number of tokens.  Host-only except for one query of
+ * the device's compute-unit count (cached per device).
  */
 size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens);
 
@@ -182,8 +184,9 @@ size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t 
  * the original indices).  Benchmark-only: it lets those paths be timed end to
  * end against mla_decode_fp8.
  *
- * Computes exactly what mla_decode_fp8 computes with K[t,:] = scale *
- * kv[kv_indices[t], :] read as BF16 instead of E4M3FN.
+ * Computes what mla_decode_fp8 computes, with the same arithmetic (BF16
+ * scores, FP16 probabilities and values in P.V, fp32 accumulation), with
+ * K[t,:] = scale * kv[kv_indices[t], :] read as BF16 instead of E4M3FN.
  *   kv          uint16 [num_rows, 576]  BF16 latent rows (e.g. the output of
  *                                       cast_pool_fp8_bf16 or gather_cast_fp8_bf16);
  *                                       values must lie within the fp16 range
@@ -228,16 +231,22 @@ size_t mla_decode_bf16_workspace_bytes(int32_t batch, int32_t num_heads, int64_t
  *   workspace   at least mla_extend_fp8_workspace_bytes(batch, num_heads,
  *               total_q) bytes of scratch (no initialisation needed,
  *               garbage afterwards; NULL allowed when total_q == 0)
- *   1 <= batch, 1 <= num_heads <= FP8MLA_MAX_HEADS, 0 <= total_q < 2^29,
+ *   1 <= batch, 1 <= num_heads <= FP8MLA_MAX_HEADS, 0 <= total_q < 2^23,
  *   total_q * num_heads <= 2^31 - 1,
  *   0 <= total_kv <= 2^31 - 1; num_slots >= 1 when total_kv > 0;
  *   scale finite > 0, sm_scale finite.
+ * Work is organised in blocks of T query tokens of one request (T = 4 for
+ * num_heads <= 16, 2 for <= 32, else 1), each reading its visible tokens in
+ * 64-token tiles.  With NB = ceil(total_q / T) the call also requires
+ *   batch + NB <= 2^25   and   (NB + 1) * ceil(total_kv / 64) + batch + NB <= 2^28,
+ * a bound on the tiles read that holds for every index layout with these
+ * sizes (e.g. a single causal prefill of up to ~128k tokens at 64 or more
+ * heads, 4x that at 16 heads); larger calls return FP8MLA_ERR_BAD_SHAPE and
+ * launch nothing.  Every accepted call writes every row of `out` it owns.
  * The index arrays are read on the device only.  Out-of-range indptr
  * entries are clamped into [0, total_q] / [0, total_kv] (a wrong row, never
- * an out-of-bounds access).  Per call, at most 2^29 (token block, visible
- * token) pairs -- sum over blocks of 4 (H <= 16), 2 (H <= 32) or 1 query
- * tokens of the block's last limit -- are supported; beyond that the call
- * leaves out unwritten.
+ * an out-of-bounds access); with a decreasing indptr every row may come out
+ * zero.
  */
 int mla_extend_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
                    const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
@@ -247,7 +256,8 @@ int mla_extend_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
 
 /* Workspace size in bytes for mla_extend_fp8 (0 when total_q == 0 or on bad
  * arguments); depends on batch, num_heads, total_q and the device's compute
- * unit count. */
+ * unit count: O(batch + total_q) bytes of per-block records plus a fixed
+ * partial-result area of two pieces per compute unit and head row. */
 size_t mla_extend_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_q);
 
 /* Static description of a status code; never NULL. */

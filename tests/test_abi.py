@@ -219,9 +219,9 @@ def test_mla_extend_validation():
     assert ext(H=0) == ERR_SHAPE
     assert ext(H=257) == ERR_SHAPE
     assert ext(tq=-1) == ERR_SHAPE
-    assert ext(tq=1 << 29) == ERR_SHAPE
+    assert ext(tq=1 << 23) == ERR_SHAPE                # query rows pack into 23 bits
     assert ext(tkv=-1) == ERR_SHAPE
-    assert ext(tq=(1 << 29) - 1, H=256) == ERR_SHAPE   # query rows past 2^31 - 1
+    assert ext(tq=(1 << 23) - 1, H=257) == ERR_SHAPE
     assert ext(tkv=1 << 31) == ERR_SHAPE
     assert ext(slots=0) == ERR_SHAPE
     assert ext(scale=0.0) == ERR_SCALAR
@@ -241,3 +241,39 @@ def test_mla_extend_validation():
     assert lib.mla_extend_fp8_workspace_bytes(0, 16, 10) == 0
     assert lib.mla_extend_fp8_workspace_bytes(1, 16, 0) == 0
     assert lib.mla_extend_fp8_workspace_bytes(1, 300, 10) == 0
+
+
+def test_mla_extend_size_bound():
+    """Calls whose tile bound, (NB + 1) * ceil(total_kv / 64) + batch + NB with
+    NB = ceil(total_q / T), exceeds 2^28 are rejected on the host with
+    BAD_SHAPE (never accepted and left unwritten); calls inside the bound get
+    past every size check (here they fail later, for want of a device)."""
+    lib = _lib()
+
+    def ext(tq, tkv, B, H):
+        return lib.mla_extend_fp8(P16, P16, 1 << 22, P16, P16, P16, tq, tkv, B, H, 1.0, 0.07, 1,
+                                  P16, P16, 1 << 40, NULL)
+
+    def bound(tq, tkv, B, H):
+        rows = -(-H // 16) * 16
+        T = 64 // rows if rows <= 64 else 1
+        nb = -(-tq // T)
+        return (nb + 1) * -(-tkv // 64) + B + nb
+
+    cases = [
+        (32768, 32768, 1, 128, True),        # 32k causal prefill, 128 heads
+        (65536, 65536, 1, 64, True),         # 64k prefill, 64 heads
+        (131072, 131072, 1, 128, False),     # 128k prefill at T = 1: bound just past 2^28
+        (131072, 131072, 1, 16, True),       # the same at 16 heads (T = 4)
+        (1024, 256 * 32768, 256, 16, True),  # 4 speculative tokens x 256 requests of 32k
+        (1 << 22, 1 << 24, 1, 64, False),
+        (1, 1, 1 << 25, 16, False),          # more virtual requests than 2^25
+    ]
+    for tq, tkv, B, H, ok in cases:
+        assert (bound(tq, tkv, B, H) <= 1 << 28) == ok or B >= 1 << 25, (tq, tkv, B, H)
+        st = ext(tq, tkv, B, H)
+        if ok:
+            assert st != ERR_SHAPE, (tq, tkv, B, H, st)
+        else:
+            assert st == ERR_SHAPE, (tq, tkv, B, H, st)
+

@@ -81,3 +81,28 @@ def test_empty(dev):
                              w.sm_scale)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out.float()).item() == 0
+
+
+@pytest.mark.parametrize("H", [16, 64, 100, 128])
+def test_outliers_and_large_scores(dev, H):
+    """1% of cache values at +-448 with queries 4 x N(0,1) and scale 2: near
+    one-hot softmax over values of opposite sign that cancel, the case in
+    which BF16 probabilities (8 significant bits) miss the tolerance."""
+    w = workloads.small(5, H, [700, 64, 65, 1, 2049], seed=60 + H, device=dev, scale=2.0,
+                        q_sigma=4.0, outlier_frac=0.01)
+    e = _check_cast_pool_path(w, "bf16 outliers H=%d" % H)
+    print("bf16 outliers H=%d" % H, e, flush=True)
+
+
+@pytest.mark.parametrize("H", [100, 128])
+def test_high_head_counts(dev, H):
+    w = workloads.small(3, H, [3000, 50, 9000], seed=H, device=dev, scale=1.3)
+    _check_cast_pool_path(w, "bf16 H=%d" % H)
+
+
+def test_config5_serving_mix_full(dev):
+    """The serving mix (256 requests, 1% +-448 outliers, q = 2 N(0,1)) through
+    the BF16 rows of its cast pool: every request against the oracle."""
+    w = workloads.config(5, device=dev)
+    e = _check_cast_pool_path(w, "bf16 config5")
+    print("bf16 config5", e, flush=True)

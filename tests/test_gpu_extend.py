@@ -1,7 +1,7 @@
 """GPU parity of the extend (prefill) attention mla_extend_fp8 against the
 float64 oracle: several query tokens per request, causal or not, ragged
 token counts, head counts on both sides of 64, blocks spanning segments,
-tokens that see nothing, and the named extend workloads (sampled rows)."""
+tokens that see nothing, and the named extend workloads (every row)."""
 import numpy as np
 import pytest
 import torch
@@ -128,11 +128,25 @@ def test_deterministic(dev):
 
 
 @pytest.mark.parametrize("name", list(workloads.EXTEND_NAMES))
-def test_named_extend_workloads_sampled(dev, name):
+def test_named_extend_workloads_full(dev, name):
+    """Every query row of the named extend workloads the benchmark times."""
     w = workloads.extend_config(name, device="cpu")
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([[0, w.total_q - 1], rng.integers(0, w.total_q, size=12)]))
-    _check(w, dev, name, rows=rows)
+    e = _check(w, dev, name)
+    print(name, e, flush=True)
+
+
+def test_prefill_past_2_29_visible_pairs(dev):
+    """A causal prefill of 32,768 tokens at 64 heads: 536,887,296 (token,
+    visible token) pairs, past 2^29, which an earlier layout of the block CSR
+    could not address.  The whole call runs; the oracle checks the rows that
+    see the most tokens (the last ones), a row from each quarter, and the
+    first."""
+    n = 32768
+    w = workloads.extend(1, 64, [n], [0], seed=77)
+    assert w.visible_tokens() > 1 << 29
+    rows = np.array([0, n // 4, n // 2, 3 * n // 4, n - 2, n - 1])
+    e = _check(w, dev, "prefill 32k H=64", rows=rows)
+    print("prefill 32k", e, flush=True)
 
 
 @pytest.mark.parametrize("H", [256, 96])
