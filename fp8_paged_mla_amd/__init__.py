@@ -37,6 +37,7 @@ __all__ = [
     "scatter_cast_bf16_fp8",
     "mla_decode_fp8",
     "mla_decode_fp8_workspace_bytes",
+    "mla_decode_fp8_noalloc",
     "mla_decode_bf16",
     "mla_extend_fp8",
     "mla_extend_fp8_workspace_bytes",
@@ -75,6 +76,8 @@ def library() -> ctypes.CDLL:
     lib.scatter_cast_bf16_fp8.restype = ctypes.c_int
     lib.mla_decode_fp8.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, f32, f32, vp, vp, sz, vp]
     lib.mla_decode_fp8.restype = ctypes.c_int
+    lib.mla_decode_fp8_noalloc.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, f32, f32, vp, vp]
+    lib.mla_decode_fp8_noalloc.restype = ctypes.c_int
     lib.mla_decode_fp8_workspace_bytes.argtypes = [i32, i32, i64]
     lib.mla_decode_fp8_workspace_bytes.restype = sz
     lib.mla_extend_fp8.argtypes = [vp, vp, i64, vp, vp, vp, i64, i64, i32, i32, f32, f32, i32,
@@ -317,6 +320,38 @@ def mla_decode_fp8(q: torch.Tensor, kv_pool: torch.Tensor, kv_indptr: torch.Tens
                                   float(scale), float(sm_scale), out.data_ptr(),
                                   workspace.data_ptr(), ws_bytes, _stream_handle(dev)),
                "mla_decode_fp8")
+    return out
+
+
+def mla_decode_fp8_noalloc(q: torch.Tensor, kv_pool: torch.Tensor, kv_indptr: torch.Tensor,
+                           kv_indices: torch.Tensor, scale: float, sm_scale: float,
+                           out: torch.Tensor) -> torch.Tensor:
+    """mla_decode_fp8 without a workspace (its split-K scratch is a static
+    array inside the library, one per GPU): for callers that cannot allocate.
+    The caller passes ``out`` [B, H, 512] bf16; nothing is allocated.  Calls
+    that may overlap on one GPU share that scratch and must not be issued."""
+    kv_pool = _pool_rows(kv_pool)
+    _require(q, "q", torch.bfloat16)
+    dev = q.device
+    _require(kv_pool, "kv_pool", None, dev)
+    _require(kv_indptr, "kv_indptr", torch.int32, dev)
+    _require(kv_indices, "kv_indices", torch.int32, dev)
+    _require(out, "out", torch.bfloat16, dev)
+    if q.dim() != 3 or q.shape[2] != KV_WIDTH:
+        raise ValueError("q must be [B, H, 576], got %s" % (tuple(q.shape),))
+    B, H = q.shape[0], q.shape[1]
+    if kv_indptr.dim() != 1 or kv_indptr.shape[0] != B + 1:
+        raise ValueError("kv_indptr must be [B+1]")
+    if kv_indices.dim() != 1:
+        raise ValueError("kv_indices must be 1-D")
+    if tuple(out.shape) != (B, H, V_WIDTH):
+        raise ValueError("out must be [%d, %d, 512]" % (B, H))
+    with torch.cuda.device(dev):
+        _check(library().mla_decode_fp8_noalloc(q.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
+                                                kv_indptr.data_ptr(), kv_indices.data_ptr(),
+                                                kv_indices.shape[0], B, H, float(scale),
+                                                float(sm_scale), out.data_ptr(), _stream_handle(dev)),
+               "mla_decode_fp8_noalloc")
     return out
 
 

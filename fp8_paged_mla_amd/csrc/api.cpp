@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/fp8mla.h"
 #include "launch.h"
@@ -53,6 +54,34 @@ int check_decode_fp8_args(const uint16_t* q, const uint8_t* kv_pool, int64_t num
   if (total_tokens > 0 && (!aligned16(kv_pool) || !aligned4(kv_indices)))
     return FP8MLA_ERR_MISALIGNED;
   return FP8MLA_OK;
+}
+
+// Split-K scratch of mla_decode_fp8_noalloc, for callers that cannot
+// allocate: one array per device, held by every GPU the library runs on
+// until the process ends, shared by all such calls on that GPU (they race
+// if they overlap).  The decode needs no initialised scratch: every word a
+// kernel reads was written earlier in the same call.  On the host `scratch`
+// is only a stand-in for the device variable, never a device address: host
+// code uses the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = FP8MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's scratch array, looked up once per
+// device with that device current; NULL on failure.
+void* current_device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
 }
 
 // Sizes an extend call accepts: every count in range, the virtual requests
@@ -201,6 +230,30 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
                                                  total_tokens, batch, num_heads, scale, sm_scale,
                                                  out, workspace, plan,
                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
+}
+
+int mla_decode_fp8_noalloc(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                           const int32_t* kv_indptr, const int32_t* kv_indices,
+                           int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
+                           float sm_scale, uint16_t* out, void* stream) {
+  const int st = check_decode_fp8_args(q, kv_pool, num_slots, kv_indptr, kv_indices, total_tokens,
+                                       batch, num_heads, scale, sm_scale, out);
+  if (st != FP8MLA_OK) return st;
+  if (batch > FP8MLA_NOALLOC_MAX_BATCH) return FP8MLA_ERR_BAD_SHAPE;
+  const int cus = current_device_cus();
+  if (cus <= 0) return FP8MLA_ERR_HIP;
+  const fp8mla::DecodePlan plan = fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus,
+                                                          fp8mla::fp8_decode_kernel(num_heads, total_tokens, cus));
+  void* ws = nullptr;
+  if (total_tokens > 0) {
+    if (plan.workspace_bytes > kScratchBytes) return FP8MLA_ERR_WORKSPACE;
+    ws = current_device_scratch();
+    if (!ws) return FP8MLA_ERR_HIP;
+  }
+  const hipError_t e = fp8mla::launch_mla_decode(q, kv_pool, num_slots, kv_indptr, kv_indices,
+                                                 total_tokens, batch, num_heads, scale, sm_scale,
+                                                 out, ws, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
 }
 

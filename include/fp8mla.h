@@ -23,7 +23,8 @@
  *  - All tensor arguments are DEVICE pointers on the current HIP device,
  *    owned by the caller, row-major and contiguous, 16-byte aligned.  The
  *    library never allocates or frees device memory and keeps no state
- *    between calls beyond a per-device compute-unit count.
+ *    between calls beyond a per-device compute-unit count (and, for
+ *    mla_decode_fp8_noalloc, a static scratch array per device).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue kernels on it and return; they never synchronise.  Kernel
  *    faults surface as errors of a later HIP call, as usual in HIP.
@@ -175,6 +176,30 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
  * the device's compute-unit count (cached per device).
  */
 size_t mla_decode_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_tokens);
+
+/*
+ * mla_decode_fp8_noalloc -- mla_decode_fp8 for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same computation, kernels and arguments
+ * as mla_decode_fp8 minus the workspace: the split-K scratch is a static
+ * device array of FP8MLA_NOALLOC_SCRATCH_BYTES inside the library, one per
+ * GPU, held from the first call on that GPU until the process ends.  The
+ * call allocates and frees nothing.  Every call on a GPU shares that GPU's
+ * array, so calls that may overlap on one GPU (different streams, or
+ * different host threads) race and must not be issued; serialise them or
+ * use mla_decode_fp8 with separate workspaces.
+ *   batch <= FP8MLA_NOALLOC_MAX_BATCH, else FP8MLA_ERR_BAD_SHAPE;
+ *   FP8MLA_ERR_WORKSPACE if the call would need more scratch than the array
+ *   holds (it is sized for every head count on devices of up to 256 compute
+ *   units); FP8MLA_ERR_HIP if the array's device address cannot be found.
+ * All other arguments, layouts, ownership and status codes as mla_decode_fp8.
+ */
+#define FP8MLA_NOALLOC_SCRATCH_BYTES (36u << 20)
+#define FP8MLA_NOALLOC_MAX_BATCH 65536
+int mla_decode_fp8_noalloc(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                           const int32_t* kv_indptr, const int32_t* kv_indices,
+                           int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
+                           float sm_scale, uint16_t* out, void* stream);
 
 /*
  * mla_decode_bf16 -- the same decode over BF16 latent rows: the attention

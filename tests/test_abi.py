@@ -277,3 +277,37 @@ def test_mla_extend_size_bound():
         else:
             assert st == ERR_SHAPE, (tq, tkv, B, H, st)
 
+
+def test_mla_decode_noalloc_validation():
+    """The allocation-free decode takes the same checks as mla_decode_fp8 (no
+    workspace argument) and rejects batches past its scratch's limit, all on
+    the host before any device call."""
+    lib = _lib()
+    text = open(HEADER).read()
+    max_batch = int(re.search(r"#define FP8MLA_NOALLOC_MAX_BATCH (\d+)", text).group(1))
+    scratch = re.search(r"#define FP8MLA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert int(scratch.group(1)) << int(scratch.group(2)) <= 64 << 20  # a modest, stated size
+
+    def dec(**kw):
+        a = dict(q=P16, pool=P16, slots=100, indptr=P16, idx=P16, total=10, B=2, H=16, scale=1.0,
+                 sm=0.07, out=P16, stream=NULL)
+        a.update(kw)
+        return lib.mla_decode_fp8_noalloc(a["q"], a["pool"], a["slots"], a["indptr"], a["idx"],
+                                          a["total"], a["B"], a["H"], a["scale"], a["sm"],
+                                          a["out"], a["stream"])
+
+    assert dec(B=0) == ERR_SHAPE
+    assert dec(B=max_batch + 1) == ERR_SHAPE
+    assert dec(H=0) == ERR_SHAPE
+    assert dec(H=257) == ERR_SHAPE
+    assert dec(total=-1) == ERR_SHAPE
+    assert dec(slots=0) == ERR_SHAPE
+    assert dec(scale=-1.0) == ERR_SCALAR
+    assert dec(sm=math.inf) == ERR_SCALAR
+    assert dec(q=NULL) == ERR_NULL
+    assert dec(out=NULL) == ERR_NULL
+    assert dec(pool=NULL) == ERR_NULL
+    assert dec(idx=NULL) == ERR_NULL
+    assert dec(q=P8) == ERR_ALIGN
+    assert dec(out=P8) == ERR_ALIGN
+    assert dec(indptr=P16 + 2) == ERR_ALIGN
