@@ -66,6 +66,8 @@ def parse_args():
                     help="time the extend (prefill) attention mla_extend_fp8 on a named workload")
     ap.add_argument("--write", action="store_true",
                     help="time the BF16 -> FP8 write path (scatter_cast_bf16_fp8) instead")
+    ap.add_argument("--probe", action="store_true",
+                    help="run the HBM ceiling probes (read, 1:2 read:write, random 576-B rows) only")
     return ap.parse_args()
 
 
@@ -104,6 +106,14 @@ def read_traffic(launch_units):
         return float(vals["hbm_bytes_per_call"])
     except (KeyError, ValueError):
         return None
+
+
+def algorithmic_decode_bytes(w):
+    """Bytes a decode call must move: every attended token's 576-byte row and
+    4-byte slot id, the indptr entries, q (576 BF16 per head) and out (512
+    BF16 per head); split-K partials are the implementation's, not the
+    method's."""
+    return (w.total_tokens * (576 + 4) + 4 * (w.B + 1) + 2 * w.B * w.H * (576 + 512))
 
 
 def cpu_baseline(w, label, budget_s=15.0):
@@ -179,6 +189,9 @@ def main():
     if args.serving_step:
         print(json.dumps(serving_step(fm, workloads, torch, dev, args)), flush=True)
         return
+    if args.probe:
+        print(json.dumps(hbm_probes(torch, dev, full=True)), flush=True)
+        return
 
     base = workloads.config(args.config, 0, device=dev)
     pool_bytes = base.pool.numel()
@@ -188,12 +201,18 @@ def main():
     wss = [torch.empty(max(256, fm.mla_decode_fp8_workspace_bytes(w.B, w.H, w.total_tokens)),
                        dtype=torch.uint8, device=dev) for w in reps]
     useful = [w.useful_kv_bytes for w in reps]
+    algo = [algorithmic_decode_bytes(w) for w in reps]
     stream = torch.cuda.current_stream(dev)
 
+    # each replica's call checked and marshalled once (the binding's prepared
+    # path); every call still goes through the C ABI's own checks and
+    # launches all of the decode's kernels
+    calls = [fm.prepare_mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale,
+                                       out=outs[r], workspace=wss[r], stream=stream)
+             for r, w in enumerate(reps)]
+
     def call(i):
-        w = reps[i % R]
-        fm.mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale,
-                          out=outs[i % R], workspace=wss[i % R])
+        calls[i % R]()
 
     for i in range(args.warmup):
         call(i)
@@ -206,6 +225,7 @@ def main():
     start.record(stream)
     for i in range(args.steps):
         call(i)
+    host_us = (time.perf_counter() - t0) * 1e6 / args.steps
     stop.record(stream)
     torch.cuda.synchronize(dev)
     wall_ms = (time.perf_counter() - t0) * 1e3
@@ -227,6 +247,8 @@ def main():
     q = np.percentile(per_call, [10, 50, 90])
 
     mean_useful = bytes_total / args.steps
+    mean_algo = sum(algo[i % R] for i in range(args.steps)) / args.steps
+    achieved = mean_algo / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -238,7 +260,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 scores / fp16 P.V, fp32 accumulate (fp8 e4m3 KV)",
         "data": "synthetic",
         "config": {
             "workload": workloads.CONFIG_NAMES[args.config],
@@ -254,20 +276,32 @@ def main():
         "us_per_call": {"p10": round(float(q[0]), 2), "median": round(float(q[1]), 2),
                         "p90": round(float(q[2]), 2)},
         "wall_ms_timed_region": round(wall_ms, 3),
+        "host_us_per_call": round(host_us, 2),
         "roofline": {
             "bound": "hbm",
-            "achieved": round(mean_useful / (ms_per_step * 1e-3) / 1e9, 2),
+            "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(mean_useful / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": read_traffic(1),
             "kernel": "one mla_decode_fp8 call: mla_split_kernel + mla_combine_kernel",
-            "algorithmic_bytes_per_call": int(mean_useful),
+            "algorithmic_bytes_per_call": int(mean_algo),
+            "algorithmic_bytes": "576 B KV + 4 B index per token, 4 B per indptr entry, "
+                                 "2 B per q (576) and out (512) element",
+            "useful_kv_bytes_per_call": int(mean_useful),
         },
     }
 
     if not args.no_secondary:
         result["secondary"] = secondary(fm, reps, outs, wss, stream, dev, args)
+        probes = hbm_probes(torch, dev)
+        result["secondary"]["hbm_probes"] = probes
+        # the same decode against the measured ceiling of its access mix
+        # (random 576-byte rows: useful bytes against the gather probe's)
+        result["roofline"]["probe_ceiling"] = {
+            "probe": "gather576_2chunk (random 576-B rows into LDS, no math)",
+            "GBps": probes["gather576_2chunk_GBps"],
+            "frac_useful": round(value / probes["gather576_2chunk_GBps"], 4)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(base, workloads.CONFIG_NAMES[args.config].split(":")[0])
     print(json.dumps(result), flush=True)
@@ -438,20 +472,35 @@ def extend_bench(fm, workloads, torch, dev, args):
     pairs = w.visible_tokens()
     flops = 2.0 * w.H * 1088 * pairs
     tflops = flops / (us * 1e-6) / 1e12
+    # algorithmic bytes: every cache row of a request once (576 B + its 4-byte
+    # slot id), both indptr arrays, q (576 BF16) and out (512 BF16) per query row
+    kv_tokens = int(w.kv_lens.sum())
+    algo_bytes = 580 * kv_tokens + 8 * (w.B + 1) + 2 * w.total_q * w.H * (576 + 512)
+    t_hbm_us = algo_bytes / (HBM_PEAK_GBPS * 1e9) * 1e6
+    t_mfma_us = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e6
+    if t_mfma_us >= t_hbm_us:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}
+    else:
+        gbs = algo_bytes / (us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBPS, 4)}
+    roof.update({"traffic": None, "t_hbm_us_at_peak": round(t_hbm_us, 2),
+                 "t_mfma_us_at_peak": round(t_mfma_us, 2), "algorithmic_bytes_per_call": algo_bytes,
+                 "flops_per_call": flops,
+                 "kernel": "one mla_extend_fp8 call: pre-pass + mla_split_h64_kernel<true> + combine"})
     return {
-        "metric": "extend attention over the FP8 cache: TFLOP/s (MFMA-bound) + us/call",
+        "metric": "extend attention over the FP8 cache: TFLOP/s + us/call",
         "value": round(tflops, 2), "unit": "TFLOP/s", "higher_is_better": True,
-        "data": "synthetic", "dtype": "bf16 (fp8 KV)", "steps": K,
+        "data": "synthetic", "dtype": "bf16 scores / fp16 P.V, fp32 accumulate (fp8 e4m3 KV)",
+        "steps": K,
         "config": {"workload": w.name, "total_q": w.total_q, "heads": w.H,
-                   "cache_tokens": int(w.kv_lens.sum()), "visible_pairs": pairs,
+                   "cache_tokens": kv_tokens, "visible_pairs": pairs,
                    "causal": w.causal},
         "us_per_call": round(us, 2),
         "query_tokens_per_s": round(w.total_q / (us * 1e-6), 1),
         "cache_GBps": round(w.kv_bytes() / (us * 1e-6) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
-                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "one mla_extend_fp8 call: pre-pass + mla_split_h64_kernel<true> + combine"},
+        "roofline": roof,
         "per_token_decode_us": round(us_tok, 2),
         "speedup_vs_per_token_decode": round(us_tok / us, 2),
     }
@@ -624,6 +673,87 @@ def write_path(fm, workloads, torch, dev, sizes=(40, 1024, 16384, 65536)):
             "torch_copy_then_index_us_eager": round(us_t, 2),
             "speedup_eager_vs_torch_path": round(us_t / us_e, 2)}
         del srcs, slots, longs
+    return res
+
+
+def hbm_probes(torch, dev, full=False):
+    """Measured HBM ceilings for the library's access mixes (the probes of
+    include/fp8mla_probe.h), each the best over a small sweep of launch
+    shapes, buffers past the 256 MB Infinity Cache:
+      read        sequential 16-byte loads over 2 GiB;
+      copy_1to2   512 MiB read, each 16-byte chunk written twice (1 GiB): the cast's mix;
+      write       1 GiB of sequential stores;
+      gather576   2^20 random 576-byte rows of a 2^21-slot pool into LDS, 1 or 2
+                  chunks of 16 rows in flight per wave (2: the decode's LDS budget).
+    GB/s counts bytes read + written; the gather counts 576 B per row."""
+    import numpy as np
+    from fp8_paged_mla_amd import probe
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = torch.cuda.current_stream(dev)
+    sink = torch.zeros(65536 * 8, dtype=torch.int32, device=dev)
+
+    def best_us(fn, reps=5):
+        for _ in range(2):
+            fn()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            times.append(e0.elapsed_time(e1) * 1e3)
+        return min(times)
+
+    res = {}
+    src = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    src.fill_(0x3C)
+    sweep = [(g, u) for g in (4 * cus, 8 * cus, 16 * cus) for u in (4, 8, 16)] if full else \
+            [(8 * cus, 8), (16 * cus, 8)]
+    best = None
+    for g, u in sweep:
+        us = best_us(lambda: probe.probe_read(src, g, u, sink))
+        gbs = src.numel() / (us * 1e-6) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, g, u)
+    res["read_GBps"] = round(best[0], 1)
+    res["read_launch"] = "grid %d x 256 lanes, %d loads in flight per lane" % (best[1], best[2])
+    del src
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(0x3C)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    best = None
+    for g, u in sweep:
+        us = best_us(lambda: probe.probe_copy_1to2(src, dst, g, u))
+        gbs = 3 * src.numel() / (us * 1e-6) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, g, u)
+    res["copy_1to2_GBps"] = round(best[0], 1)
+    res["copy_1to2_launch"] = "grid %d x 256 lanes, %d loads in flight per lane" % (best[1], best[2])
+    best = None
+    for g, u in sweep:
+        us = best_us(lambda: probe.probe_write(dst, g, u))
+        gbs = dst.numel() / (us * 1e-6) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, g, u)
+    res["write_GBps"] = round(best[0], 1)
+    res["write_launch"] = "grid %d x 256 lanes, %d stores per lane per step" % (best[1], best[2])
+    del src, dst
+    slots = 1 << 21
+    pool = torch.randint(0, 256, (slots, 576), dtype=torch.uint8, device=dev)
+    rng = np.random.default_rng(7)
+    idx = torch.from_numpy(rng.permutation(slots)[: 1 << 20].astype(np.int32)).to(dev)
+    for s_inflight, grids in ((2, (cus,)), (1, (cus, 2 * cus))):
+        best = None
+        for g in grids:
+            us = best_us(lambda: probe.probe_gather_rows(pool, idx, g, s_inflight, sink))
+            gbs = 576 * idx.numel() / (us * 1e-6) / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, g)
+        res["gather576_%dchunk_GBps" % s_inflight] = round(best[0], 1)
+        res["gather576_%dchunk_launch" % s_inflight] = (
+            "grid %d x 8 waves, %d x 16 rows (%d B of LDS) in flight per wave"
+            % (best[1], s_inflight, s_inflight * 9472))
+    del pool, idx
     return res
 
 

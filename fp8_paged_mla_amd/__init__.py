@@ -23,7 +23,7 @@ import os
 
 import torch
 
-from .build import LIB_PATH
+from .build import DEBUG_LIB_PATH, LIB_PATH
 
 KV_WIDTH = 576
 V_WIDTH = 512
@@ -38,14 +38,29 @@ __all__ = [
     "mla_decode_fp8",
     "mla_decode_fp8_workspace_bytes",
     "mla_decode_fp8_noalloc",
+    "prepare_mla_decode_fp8",
+    "PreparedCall",
     "mla_decode_bf16",
     "mla_extend_fp8",
     "mla_extend_fp8_workspace_bytes",
     "mla_decode_bf16_workspace_bytes",
     "status_string",
+    "check_indices",
+    "debug_status",
+    "CHECK_INDPTR_START",
+    "CHECK_INDPTR_ORDER",
+    "CHECK_INDPTR_END",
+    "CHECK_SLOT_RANGE",
     "KV_WIDTH",
     "V_WIDTH",
 ]
+
+
+# flags of check_indices / debug_status (fp8mla.h FP8MLA_CHECK_*)
+CHECK_INDPTR_START = 1
+CHECK_INDPTR_ORDER = 2
+CHECK_INDPTR_END = 4
+CHECK_SLOT_RANGE = 8
 
 
 class FP8MLAError(RuntimeError):
@@ -55,18 +70,37 @@ class FP8MLAError(RuntimeError):
 
 
 _LIB = None
+_DEBUG_LIB = None
 
 
-def library() -> ctypes.CDLL:
-    """The loaded libfp8mla.so (raises if it has not been built)."""
-    global _LIB
-    if _LIB is not None:
+def library(debug: bool = None) -> ctypes.CDLL:
+    """The loaded libfp8mla.so (raises if it has not been built).
+
+    ``debug=True`` loads the debug build libfp8mla_debug.so instead (same
+    ABI; every reading call checks the index contract on the device first, see
+    debug_status); by default the debug build is used when the environment
+    sets FP8MLA_DEBUG=1."""
+    global _LIB, _DEBUG_LIB
+    if debug is None:
+        debug = os.environ.get("FP8MLA_DEBUG", "0") == "1"
+    if debug and _DEBUG_LIB is not None:
+        return _DEBUG_LIB
+    if not debug and _LIB is not None:
         return _LIB
-    if not os.path.exists(LIB_PATH):
+    path = DEBUG_LIB_PATH if debug else LIB_PATH
+    if not os.path.exists(path):
         raise RuntimeError(
-            "libfp8mla.so is not built (%s missing); run `python -m fp8_paged_mla_amd.build`"
-            % LIB_PATH)
-    lib = ctypes.CDLL(LIB_PATH)
+            "%s is not built (%s missing); run `python -m fp8_paged_mla_amd.build`"
+            % (os.path.basename(path), path))
+    lib = _bind(ctypes.CDLL(path))
+    if debug:
+        _DEBUG_LIB = lib
+    else:
+        _LIB = lib
+    return lib
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     lib.cast_pool_fp8_bf16.argtypes = [vp, i64, vp, vp]
     lib.cast_pool_fp8_bf16.restype = ctypes.c_int
@@ -89,11 +123,14 @@ def library() -> ctypes.CDLL:
     lib.mla_decode_bf16.restype = ctypes.c_int
     lib.mla_decode_bf16_workspace_bytes.argtypes = [i32, i32, i64]
     lib.mla_decode_bf16_workspace_bytes.restype = sz
+    lib.fp8mla_check_indices.argtypes = [vp, i32, i64, vp, i64, vp, vp]
+    lib.fp8mla_check_indices.restype = ctypes.c_int
+    lib.fp8mla_debug_status.argtypes = [vp, i32]
+    lib.fp8mla_debug_status.restype = ctypes.c_int
     lib.fp8mla_status_string.argtypes = [ctypes.c_int]
     lib.fp8mla_status_string.restype = ctypes.c_char_p
     lib.fp8mla_abi_version.argtypes = []
     lib.fp8mla_abi_version.restype = ctypes.c_int
-    _LIB = lib
     return lib
 
 
@@ -355,6 +392,75 @@ def mla_decode_fp8_noalloc(q: torch.Tensor, kv_pool: torch.Tensor, kv_indptr: to
     return out
 
 
+class PreparedCall:
+    """One library call whose arguments were checked and marshalled once.
+
+    Calling it re-issues the same C-ABI call on the same buffers (whose
+    contents may change between calls) and stream, with no per-call Python
+    argument handling: for serving loops and small calls, where the
+    binding's own checks would otherwise cost more host time than the GPU
+    spends.  The library still validates every call on the host.  The
+    tensors are kept alive by the object."""
+
+    def __init__(self, fn, args, keep, result, where):
+        self._fn = fn
+        self._args = args
+        self._keep = keep
+        self.result = result
+        self._where = where
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise FP8MLAError(st, self._where)
+        return self.result
+
+
+def prepare_mla_decode_fp8(q: torch.Tensor, kv_pool: torch.Tensor, kv_indptr: torch.Tensor,
+                           kv_indices: torch.Tensor, scale: float, sm_scale: float,
+                           out: torch.Tensor = None, workspace: torch.Tensor = None,
+                           stream=None) -> PreparedCall:
+    """mla_decode_fp8 with its arguments checked and marshalled once; returns
+    a callable that enqueues the call (on ``stream``, default the current
+    stream at preparation) and returns ``out``."""
+    kv_pool = _pool_rows(kv_pool)
+    _require(q, "q", torch.bfloat16)
+    dev = q.device
+    _require(kv_pool, "kv_pool", None, dev)
+    _require(kv_indptr, "kv_indptr", torch.int32, dev)
+    _require(kv_indices, "kv_indices", torch.int32, dev)
+    if q.dim() != 3 or q.shape[2] != KV_WIDTH:
+        raise ValueError("q must be [B, H, 576], got %s" % (tuple(q.shape),))
+    B, H = q.shape[0], q.shape[1]
+    if kv_indptr.dim() != 1 or kv_indptr.shape[0] != B + 1:
+        raise ValueError("kv_indptr must be [B+1]")
+    if kv_indices.dim() != 1:
+        raise ValueError("kv_indices must be 1-D")
+    total = kv_indices.shape[0]
+    if out is None:
+        out = torch.empty((B, H, V_WIDTH), dtype=torch.bfloat16, device=dev)
+    _require(out, "out", torch.bfloat16, dev)
+    if tuple(out.shape) != (B, H, V_WIDTH):
+        raise ValueError("out must be [%d, %d, 512]" % (B, H))
+    lib = library()
+    with torch.cuda.device(dev):
+        need = int(lib.mla_decode_fp8_workspace_bytes(B, H, total))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        _require(workspace, "workspace", torch.uint8, dev)
+        if workspace.numel() < need:
+            raise ValueError("workspace needs %d bytes" % need)
+        handle = _stream_handle(dev) if stream is None else stream.cuda_stream
+    c = ctypes
+    args = (c.c_void_p(q.data_ptr()), c.c_void_p(kv_pool.data_ptr()), c.c_int64(kv_pool.shape[0]),
+            c.c_void_p(kv_indptr.data_ptr()), c.c_void_p(kv_indices.data_ptr()), c.c_int64(total),
+            c.c_int32(B), c.c_int32(H), c.c_float(float(scale)), c.c_float(float(sm_scale)),
+            c.c_void_p(out.data_ptr()), c.c_void_p(workspace.data_ptr()),
+            c.c_size_t(workspace.numel()), c.c_void_p(handle))
+    return PreparedCall(lib.mla_decode_fp8, args, (q, kv_pool, kv_indptr, kv_indices, out, workspace),
+                        out, "mla_decode_fp8")
+
+
 def mla_decode_bf16_workspace_bytes(batch: int, num_heads: int, total_tokens: int,
                                     device=None) -> int:
     dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
@@ -405,3 +511,54 @@ def mla_decode_bf16(q: torch.Tensor, kv: torch.Tensor, kv_indptr: torch.Tensor,
                                    out.data_ptr(), workspace.data_ptr(), workspace.numel(),
                                    _stream_handle(dev)), "mla_decode_bf16")
     return out
+
+
+def check_indices(indptr: torch.Tensor = None, indices: torch.Tensor = None, num_slots: int = 0,
+                  total: int = None, status: torch.Tensor = None) -> torch.Tensor:
+    """On-device check of an index layout (fp8mla_check_indices): indptr
+    [B+1] int32 starts at 0, never decreases and ends at ``total`` (default
+    len(indices)); every slot id lies in [0, num_slots).  Either array may be
+    None.  Returns the device int32 [4] status: FP8MLA_CHECK_* flags (0 = the
+    contract holds), first bad request, first bad slot position (INT32_MAX
+    when none), number of bad slot ids."""
+    ref = indptr if indptr is not None else indices
+    if ref is None:
+        raise ValueError("give indptr, indices or both")
+    dev = ref.device
+    B = 0
+    if indptr is not None:
+        _require(indptr, "indptr", torch.int32, dev)
+        if indptr.dim() != 1 or indptr.shape[0] < 2:
+            raise ValueError("indptr must be [B+1] with B >= 1")
+        B = indptr.shape[0] - 1
+    if indices is not None:
+        _require(indices, "indices", torch.int32, dev)
+        if indices.dim() != 1:
+            raise ValueError("indices must be 1-D")
+    if total is None:
+        if indices is None:
+            raise ValueError("total is needed without indices")
+        total = indices.shape[0]
+    if indices is not None and indices.shape[0] < total:
+        raise ValueError("indices holds fewer than total entries")
+    if status is None:
+        status = torch.empty(4, dtype=torch.int32, device=dev)
+    _require(status, "status", torch.int32, dev)
+    with torch.cuda.device(dev):
+        _check(library().fp8mla_check_indices(
+            indptr.data_ptr() if indptr is not None else None, B, int(total),
+            indices.data_ptr() if indices is not None else None, int(num_slots),
+            status.data_ptr(), _stream_handle(dev)), "fp8mla_check_indices")
+    return status
+
+
+def debug_status(reset: bool = False, device=None) -> list:
+    """The debug build's accumulated index-check status on ``device`` (waits
+    for the device to finish): [flags, first bad request, first bad slot
+    position, bad slot count].  Raises on the release build."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    out = (ctypes.c_int32 * 4)()
+    with torch.cuda.device(dev):
+        _check(library(debug=True).fp8mla_debug_status(ctypes.cast(out, ctypes.c_void_p),
+                                                       1 if reset else 0), "fp8mla_debug_status")
+    return [int(v) for v in out]

@@ -1,9 +1,13 @@
-"""Build libfp8mla.so in-tree with hipcc for gfx950.
+"""Build libfp8mla.so (and its debug build libfp8mla_debug.so) in-tree with
+hipcc for gfx950.
 
     python -m fp8_paged_mla_amd.build [-v]
 
 Each HIP/C++ translation unit is compiled in parallel into ``_build/`` at the
-repository root, then linked into ``fp8_paged_mla_amd/libfp8mla.so``.
+repository root, then linked into ``fp8_paged_mla_amd/libfp8mla.so``.  The
+debug build differs only in the C ABI unit (``api.cpp`` compiled with
+``FP8MLA_DEBUG_CHECKS``: every reading call first checks the index contract
+on the device) and is linked into ``fp8_paged_mla_amd/libfp8mla_debug.so``.
 """
 import concurrent.futures
 import os
@@ -17,9 +21,11 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libfp8mla.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+DEBUG_LIB_PATH = os.path.join(PKG_DIR, "libfp8mla_debug.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "cast.hip", "scatter_cast.hip", "mla_decode.hip", "mla_decode_h64.hip", "mla_decode_bf16.hip", "mla_extend.hip"]
+SOURCES = ["api.cpp", "cast.hip", "scatter_cast.hip", "mla_decode.hip", "mla_decode_h64.hip",
+           "mla_decode_bf16.hip", "mla_extend.hip", "index_check.hip", "hbm_probe.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-fPIC", "-std=c++17", "-Wall",
@@ -39,9 +45,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libfp8mla.so)")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON_FLAGS + HIP_FLAGS
+def _compile(job, verbose: bool) -> str:
+    src, obj_name, extra = job
+    obj = os.path.join(BUILD_DIR, obj_name)
+    cmd = [hipcc()] + COMMON_FLAGS + HIP_FLAGS + list(extra)
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -57,19 +64,30 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path, verbose: bool) -> str:
+    tmp = path + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("linking %s failed:\n%s%s" % (LIB_NAME, res.stdout, res.stderr))
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError("linking %s failed:\n%s%s" % (os.path.basename(path), res.stdout,
+                                                         res.stderr))
+    os.replace(tmp, path)
+    return path
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link both shared libraries; returns the
+    release library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = [(s, os.path.basename(s) + ".o", ()) for s in SOURCES]
+    jobs.append(("api.cpp", "api_debug.cpp.o", ("-DFP8MLA_DEBUG_CHECKS",)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(j, verbose), jobs))
+    release, debug_api = objs[:-1], objs[-1]
+    _link(release, LIB_PATH, verbose)
+    _link([debug_api] + release[1:], DEBUG_LIB_PATH, verbose)
     return LIB_PATH
 
 

@@ -84,6 +84,44 @@ void* current_device_scratch() {
   return ptr;
 }
 
+#ifdef FP8MLA_DEBUG_CHECKS
+// Debug build: every reading call first runs the index-contract check into
+// this sticky per-device status (flags, first bad request, first bad slot
+// position, bad slot count), read and cleared by fp8mla_debug_status.  Host
+// code uses the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(16) int32_t debug_status[4] = {0, INT32_MAX, INT32_MAX, 0};
+std::atomic<int32_t*> g_debug_status_ptr[kMaxDevices];
+
+int32_t* current_device_debug_status() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  int32_t* ptr = g_debug_status_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  ptr = g_debug_status_ptr[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(debug_status)) != hipSuccess || !p) return nullptr;
+    ptr = static_cast<int32_t*>(p);
+    g_debug_status_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+hipError_t debug_check(const int32_t* indptr, int32_t batch, int64_t total, const int32_t* indices,
+                       int64_t num_slots, int cus, void* stream) {
+  int32_t* st = current_device_debug_status();
+  if (!st) return hipErrorInvalidSymbol;
+  return fp8mla::launch_index_check(indptr, batch, total, indices, num_slots, st, false, cus,
+                                    static_cast<hipStream_t>(stream));
+}
+#else
+// Release build: no checks on the reading calls' path.
+hipError_t debug_check(const int32_t*, int32_t, int64_t, const int32_t*, int64_t, int, void*) {
+  return hipSuccess;
+}
+#endif
+
 // Sizes an extend call accepts: every count in range, the virtual requests
 // and the tile bound of their CSR within what the kernels address.
 bool extend_sizes_ok(int32_t batch, int32_t num_heads, int64_t total_q, int64_t total_kv) {
@@ -112,8 +150,45 @@ const char* fp8mla_status_string(int status) {
     case FP8MLA_ERR_WORKSPACE: return "workspace missing or too small";
     case FP8MLA_ERR_BAD_SCALAR: return "scale / inv_scale must be finite and > 0, sm_scale finite";
     case FP8MLA_ERR_HIP: return "HIP runtime error or kernel launch failure";
+    case FP8MLA_ERR_NOT_DEBUG: return "not the debug build (no accumulated check status)";
     default: return "unknown status";
   }
+}
+
+int fp8mla_check_indices(const int32_t* indptr, int32_t batch, int64_t total,
+                         const int32_t* indices, int64_t num_slots, int32_t* status,
+                         void* stream) {
+  if (total < 0 || total > kMaxTokens || (indptr && (batch < 1 || batch == INT32_MAX)) ||
+      (indices && (num_slots < 1 || num_slots > kMaxSlots)))
+    return FP8MLA_ERR_BAD_SHAPE;
+  if (!status) return FP8MLA_ERR_NULL_PTR;
+  if (!aligned4(status) || (indptr && !aligned4(indptr)) || (indices && !aligned4(indices)))
+    return FP8MLA_ERR_MISALIGNED;
+  const int cus = current_device_cus();
+  if (cus <= 0) return FP8MLA_ERR_HIP;
+  const hipError_t e = fp8mla::launch_index_check(indptr, batch, total, indices, num_slots, status,
+                                                  true, cus, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
+}
+
+int fp8mla_debug_status(int32_t* status_out, int32_t reset) {
+#ifdef FP8MLA_DEBUG_CHECKS
+  if (!status_out) return FP8MLA_ERR_NULL_PTR;
+  int32_t* st = current_device_debug_status();
+  if (!st) return FP8MLA_ERR_HIP;
+  if (hipDeviceSynchronize() != hipSuccess) return FP8MLA_ERR_HIP;
+  if (hipMemcpy(status_out, st, 4 * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+    return FP8MLA_ERR_HIP;
+  if (reset) {
+    const int32_t init[4] = {0, INT32_MAX, INT32_MAX, 0};
+    if (hipMemcpy(st, init, sizeof(init), hipMemcpyHostToDevice) != hipSuccess) return FP8MLA_ERR_HIP;
+  }
+  return FP8MLA_OK;
+#else
+  (void)status_out;
+  (void)reset;
+  return FP8MLA_ERR_NOT_DEBUG;
+#endif
 }
 
 int cast_pool_fp8_bf16(const uint8_t* pool, int64_t num_slots, uint16_t* out, void* stream) {
@@ -138,6 +213,8 @@ int gather_cast_fp8_bf16(const uint8_t* pool, int64_t num_slots, const int32_t* 
   if (!aligned16(pool) || !aligned16(out) || !aligned4(indices)) return FP8MLA_ERR_MISALIGNED;
   const int cus = current_device_cus();
   if (cus <= 0) return FP8MLA_ERR_HIP;
+  if (debug_check(nullptr, 0, n, indices, num_slots, cus, stream) != hipSuccess)
+    return FP8MLA_ERR_HIP;
   const hipError_t e = fp8mla::launch_gather_cast(pool, num_slots, indices, n, out,
                                                   static_cast<hipStream_t>(stream), cus);
   return e == hipSuccess ? FP8MLA_OK : FP8MLA_ERR_HIP;
@@ -193,6 +270,9 @@ int mla_extend_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
   if (cus <= 0) return FP8MLA_ERR_HIP;
   const fp8mla::ExtendPlan plan = fp8mla::plan_mla_extend(batch, num_heads, total_q, cus);
   if (workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
+  if (debug_check(qo_indptr, batch, total_q, nullptr, 0, cus, stream) != hipSuccess ||
+      debug_check(kv_indptr, batch, total_kv, kv_indices, num_slots, cus, stream) != hipSuccess)
+    return FP8MLA_ERR_HIP;
   const hipError_t e = fp8mla::launch_mla_extend(q, kv_pool, num_slots, qo_indptr, kv_indptr,
                                                  kv_indices, total_q, total_kv, batch, num_heads,
                                                  scale, sm_scale, causal != 0, out, workspace,
@@ -226,6 +306,8 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
   const fp8mla::DecodePlan plan = fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus,
                                                           fp8mla::fp8_decode_kernel(num_heads, total_tokens, cus));
   if (total_tokens > 0 && workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
+  if (debug_check(kv_indptr, batch, total_tokens, kv_indices, num_slots, cus, stream) != hipSuccess)
+    return FP8MLA_ERR_HIP;
   const hipError_t e = fp8mla::launch_mla_decode(q, kv_pool, num_slots, kv_indptr, kv_indices,
                                                  total_tokens, batch, num_heads, scale, sm_scale,
                                                  out, workspace, plan,
@@ -251,6 +333,8 @@ int mla_decode_fp8_noalloc(const uint16_t* q, const uint8_t* kv_pool, int64_t nu
     ws = current_device_scratch();
     if (!ws) return FP8MLA_ERR_HIP;
   }
+  if (debug_check(kv_indptr, batch, total_tokens, kv_indices, num_slots, cus, stream) != hipSuccess)
+    return FP8MLA_ERR_HIP;
   const hipError_t e = fp8mla::launch_mla_decode(q, kv_pool, num_slots, kv_indptr, kv_indices,
                                                  total_tokens, batch, num_heads, scale, sm_scale,
                                                  out, ws, plan, static_cast<hipStream_t>(stream));
@@ -287,6 +371,8 @@ int mla_decode_bf16(const uint16_t* q, const uint16_t* kv, int64_t num_rows,
   const fp8mla::DecodePlan plan =
       fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus, fp8mla::DecodeKernel::kBf16);
   if (total_tokens > 0 && workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
+  if (debug_check(kv_indptr, batch, total_tokens, kv_indices, num_rows, cus, stream) != hipSuccess)
+    return FP8MLA_ERR_HIP;
   const hipError_t e = fp8mla::launch_mla_decode_bf16(q, kv, num_rows, kv_indptr, kv_indices,
                                                       total_tokens, batch, num_heads, scale,
                                                       sm_scale, out, workspace, plan,

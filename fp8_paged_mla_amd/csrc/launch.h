@@ -128,6 +128,22 @@ hipError_t launch_mla_extend(const uint16_t* q, const uint8_t* kv_pool, int64_t 
                              bool causal, uint16_t* out, void* workspace, const ExtendPlan& plan,
                              hipStream_t stream);
 
+// Contract check of a request CSR and its slot ids (status int32[4], see
+// fp8mla_check_indices); indptr or indices may be NULL to skip that part.
+hipError_t launch_index_check(const int32_t* indptr, int32_t batch, int64_t total,
+                              const int32_t* indices, int64_t num_slots, int32_t* status,
+                              bool reset, int num_cus, hipStream_t stream);
+
+// HBM ceiling probes (benchmark-only).
+hipError_t launch_probe_read(const void* src, int64_t bytes, int grid, int unroll, uint32_t* sink,
+                             hipStream_t stream);
+hipError_t launch_probe_copy12(const void* src, int64_t bytes, void* dst, int grid, int unroll,
+                               hipStream_t stream);
+hipError_t launch_probe_write(void* dst, int64_t bytes, int grid, int unroll, hipStream_t stream);
+hipError_t launch_probe_gather(const uint8_t* pool, int64_t num_slots, const int32_t* idx,
+                               int64_t n, int grid, int chunks_in_flight, uint32_t* sink,
+                               hipStream_t stream);
+
 constexpr int kFp8TileTokens = 128;
 constexpr int kH64TileTokens = 64;
 constexpr int kBf16TileTokens = 64;

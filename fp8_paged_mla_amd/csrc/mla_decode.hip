@@ -448,6 +448,15 @@ DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_token
   const int64_t max_tiles =
       (total_tokens > 0 ? (total_tokens + tile_tokens - 1) / tile_tokens : 0) + batch;
   if (nseg > max_tiles) nseg = max_tiles;
+  if (batch == 1 && total_tokens > 0) {
+    // one request: its tile count is known, and so is the split's own cap on
+    // segments (every segment holds at least TILE_W + START_W of the total
+    // weight 4 t + 2); a single segment needs no merge, so the combine kernel
+    // is not launched
+    const int64_t t = (total_tokens + tile_tokens - 1) / tile_tokens;
+    const int64_t cap = (decode::TILE_W * t + decode::START_W) / (decode::TILE_W + decode::START_W);
+    if (nseg > cap) nseg = cap;
+  }
   if (nseg < 1) nseg = 1;
   pl.nseg = (int32_t)nseg;
   pl.items = pl.nseg * pl.HG;
@@ -541,7 +550,8 @@ hipError_t launch_mla_decode(const uint16_t* q, const uint8_t* kv_pool, int64_t 
   else
     hipLaunchKernelGGL(mla_split_kernel<false>, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || total_tokens == 0) return e;  // no tokens: nothing to merge
+  // no tokens, or one segment (every request complete in it): nothing to merge
+  if (e != hipSuccess || total_tokens == 0 || pl.nseg == 1) return e;
   return launch_mla_combine(sp, stream);
 }
 

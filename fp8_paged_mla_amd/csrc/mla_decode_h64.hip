@@ -425,7 +425,8 @@ hipError_t launch_mla_decode_h64(const uint16_t* q, const uint8_t* kv_pool, int6
                                                    sm_scale, out, workspace, pl);
   hipLaunchKernelGGL(mla_split_h64_kernel<false>, dim3(pl.grid), dim3(THREADS), 0, stream, sp);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || total_tokens == 0) return e;
+  // no tokens, or one segment (every request complete in it): nothing to merge
+  if (e != hipSuccess || total_tokens == 0 || pl.nseg == 1) return e;
   return launch_mla_combine(sp, stream);
 }
 

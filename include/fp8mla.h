@@ -61,6 +61,7 @@ extern "C" {
 #define FP8MLA_ERR_WORKSPACE (-4)       /* workspace NULL or smaller than required         */
 #define FP8MLA_ERR_BAD_SCALAR (-5)      /* a scale not finite, or scale / inv_scale <= 0   */
 #define FP8MLA_ERR_HIP (-6)             /* a HIP runtime call or kernel launch failed      */
+#define FP8MLA_ERR_NOT_DEBUG (-7)       /* fp8mla_debug_status called on the release build */
 
 /*
  * cast_pool_fp8_bf16 -- the full-pool cast the pages measured
@@ -284,6 +285,51 @@ int mla_extend_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
  * unit count: O(batch + total_q) bytes of per-block records plus a fixed
  * partial-result area of two pieces per compute unit and head row. */
 size_t mla_extend_fp8_workspace_bytes(int32_t batch, int32_t num_heads, int64_t total_q);
+
+/*
+ * fp8mla_check_indices -- on-device check of the index contract that the
+ * reading calls assume but cannot afford to verify on their hot path.  They
+ * clamp out-of-range entries (a wrong row, never an out-of-bounds access),
+ * so a broken layout would otherwise fail silently -- the failure mode "The
+ * KV Cache Cast Bottleneck" warns about (Assumptions, assumption 5: a
+ * fallback that silently does nothing masks configuration errors).
+ *
+ * Checks, on the device, without a host read of the arrays:
+ *   indptr[0] == 0, indptr[b] <= indptr[b+1], indptr[batch] == total, and
+ *   0 <= indices[i] < num_slots for i < total.
+ *   indptr    int32 [batch + 1] (NULL: only the slot ids are checked, as for
+ *             gather_cast_fp8_bf16's index list)
+ *   indices   int32 [total] (NULL: only indptr is checked, as for an extend
+ *             call's qo_indptr against total_q)
+ *   status    int32 [4] on the device, written: [0] FP8MLA_CHECK_* flags (0 =
+ *             contract holds), [1] first request b with indptr[b+1] <
+ *             indptr[b], [2] first position of an out-of-range slot id (both
+ *             INT32_MAX if none), [3] number of out-of-range slot ids.
+ * batch >= 1 when indptr is given; 0 <= total <= 2^31 - 1; num_slots >= 1
+ * when indices are given.  Enqueues small kernels on `stream`, no sync.
+ *
+ * Debug build.  The library built with FP8MLA_DEBUG=1 (libfp8mla_debug.so,
+ * same ABI) runs these checks inside every reading call -- mla_decode_fp8,
+ * mla_decode_fp8_noalloc, mla_decode_bf16, mla_extend_fp8 (qo_indptr against
+ * total_q, kv_indptr and kv_indices against total_kv) and
+ * gather_cast_fp8_bf16 -- before its own kernels, accumulating into one
+ * sticky status per device that fp8mla_debug_status reads.
+ */
+#define FP8MLA_CHECK_INDPTR_START 1  /* indptr[0] != 0                        */
+#define FP8MLA_CHECK_INDPTR_ORDER 2  /* indptr decreases somewhere            */
+#define FP8MLA_CHECK_INDPTR_END 4    /* indptr[batch] != total                */
+#define FP8MLA_CHECK_SLOT_RANGE 8    /* a slot id outside [0, num_slots)      */
+int fp8mla_check_indices(const int32_t* indptr, int32_t batch, int64_t total,
+                         const int32_t* indices, int64_t num_slots, int32_t* status,
+                         void* stream);
+
+/*
+ * fp8mla_debug_status -- debug build only: waits for the current device to
+ * finish all work, copies its accumulated check status (layout as above)
+ * into host memory status_out[4], and if `reset` clears it.  The release
+ * build returns FP8MLA_ERR_NOT_DEBUG.
+ */
+int fp8mla_debug_status(int32_t* status_out, int32_t reset);
 
 /* Static description of a status code; never NULL. */
 const char* fp8mla_status_string(int status);

@@ -9,6 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp8mla.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "fp8mla_probe.h")
 
 fm = pytest.importorskip("fp8_paged_mla_amd")
 
@@ -20,8 +21,8 @@ def _lib():
         pytest.fail(str(e))
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
 
@@ -311,3 +312,57 @@ def test_mla_decode_noalloc_validation():
     assert dec(q=P8) == ERR_ALIGN
     assert dec(out=P8) == ERR_ALIGN
     assert dec(indptr=P16 + 2) == ERR_ALIGN
+
+
+def test_probe_header_symbols_exported_and_validated():
+    """The HBM probes' header: every declared call is exported, and bad
+    arguments are rejected on the host."""
+    lib = _lib()
+    names = _declared_functions(PROBE_HEADER)
+    assert set(names) == {"fp8mla_probe_read", "fp8mla_probe_copy_1to2", "fp8mla_probe_write",
+                          "fp8mla_probe_gather_rows"}
+    for n in names:
+        assert hasattr(lib, n), n
+    from fp8_paged_mla_amd import probe
+    L = probe._lib()
+    assert L.fp8mla_probe_read(P16, 0, 256, 8, P16, NULL) == ERR_SHAPE
+    assert L.fp8mla_probe_read(P16, 1000, 256, 8, P16, NULL) == ERR_SHAPE   # not a multiple of 16
+    assert L.fp8mla_probe_read(P16, 1024, 0, 8, P16, NULL) == ERR_SHAPE
+    assert L.fp8mla_probe_read(P16, 1024, 256, 5, P16, NULL) == ERR_SHAPE
+    assert L.fp8mla_probe_read(NULL, 1024, 256, 8, P16, NULL) == ERR_NULL
+    assert L.fp8mla_probe_read(P8, 1024, 256, 8, P16, NULL) == ERR_ALIGN
+    assert L.fp8mla_probe_copy_1to2(P16, 1024, NULL, 256, 8, NULL) == ERR_NULL
+    assert L.fp8mla_probe_copy_1to2(P16, 1040, P16, 256, 8, NULL) == ERR_SHAPE  # not whole KB
+    assert L.fp8mla_probe_copy_1to2(P16, 1024, P8, 256, 8, NULL) == ERR_ALIGN
+    assert L.fp8mla_probe_write(P16, 0, 256, 8, NULL) == ERR_SHAPE
+    assert L.fp8mla_probe_write(NULL, 1024, 256, 8, NULL) == ERR_NULL
+    assert L.fp8mla_probe_write(P8, 1024, 256, 8, NULL) == ERR_ALIGN
+    assert L.fp8mla_probe_gather_rows(P16, 0, P16, 16, 256, 2, P16, NULL) == ERR_SHAPE
+    assert L.fp8mla_probe_gather_rows(P16, 100, P16, 17, 256, 2, P16, NULL) == ERR_SHAPE
+    assert L.fp8mla_probe_gather_rows(P16, 100, P16, 16, 256, 3, P16, NULL) == ERR_SHAPE
+    assert L.fp8mla_probe_gather_rows(P16, 100, NULL, 16, 256, 2, P16, NULL) == ERR_NULL
+    assert L.fp8mla_probe_gather_rows(P16, 100, P16 + 2, 16, 256, 2, P16, NULL) == ERR_ALIGN
+
+
+def test_index_check_validation_and_debug_status():
+    """fp8mla_check_indices rejects bad arguments on the host; the release
+    build has no accumulated check status, the debug build exports the same
+    ABI."""
+    lib = _lib()
+    ck = lib.fp8mla_check_indices
+    assert ck(P16, 0, 10, P16, 100, P16, NULL) == ERR_SHAPE       # batch 0 with an indptr
+    assert ck(P16, 2, -1, P16, 100, P16, NULL) == ERR_SHAPE       # negative total
+    assert ck(P16, 2, 10, P16, 0, P16, NULL) == ERR_SHAPE         # indices but no pool
+    assert ck(P16, 2, 10, P16, 100, NULL, NULL) == ERR_NULL       # no status
+    assert ck(P16 + 2, 2, 10, P16, 100, P16, NULL) == ERR_ALIGN
+    assert ck(P16, 2, 10, P16 + 1, 100, P16, NULL) == ERR_ALIGN
+    assert ck(P16, 2, 10, P16, 100, P16 + 2, NULL) == ERR_ALIGN
+    out = (ctypes.c_int32 * 4)()
+    not_debug = _status("FP8MLA_ERR_NOT_DEBUG")
+    assert not_debug == -7
+    assert lib.fp8mla_debug_status(ctypes.cast(out, ctypes.c_void_p), 0) == not_debug
+    assert "debug" in fm.status_string(not_debug)
+    dbg = fm.library(debug=True)
+    for name in _declared_functions():
+        assert hasattr(dbg, name), name
+    assert dbg.fp8mla_debug_status(None, 0) == ERR_NULL

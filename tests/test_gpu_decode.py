@@ -238,3 +238,28 @@ def test_workspace_size_does_not_grow_with_tokens(dev):
     for B, H in [(1, 16), (40, 16), (8, 128), (256, 16), (3, 100), (2, 64)]:
         sizes = {fm.mla_decode_fp8_workspace_bytes(B, H, n, dev) for n in [1, 1000, 10 ** 6, 10 ** 9]}
         assert len(sizes) == 1, (B, H, sizes)
+
+
+def test_prepared_call_reuses_buffers(dev):
+    """The prepared path re-issues the same call on the same buffers: new
+    contents written into them between calls give the new results."""
+    w = workloads.small(4, 16, [900, 1, 3000, 128], seed=71, device=dev)
+    call = fm.prepare_mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale)
+    a = call().clone()
+    torch.cuda.synchronize()
+    assert_attention_close(a, oracle.mla_decode_ref(*oracle_args(w)), "prepared 1")
+    w.q.copy_(workloads.random_q(w.B, w.H, seed=72, device=dev))
+    b = call()
+    torch.cuda.synchronize()
+    assert b.data_ptr() == call.result.data_ptr()
+    assert_attention_close(b, oracle.mla_decode_ref(*oracle_args(w)), "prepared 2")
+    assert not torch.equal(a, b)
+
+
+@pytest.mark.parametrize("n", [1, 64, 128, 129, 256, 257, 400])
+def test_single_request_small_plans(dev, n):
+    """One request of up to a few tiles: the plan knows its tile count, and
+    with a single segment no combine kernel is launched."""
+    for H in (16, 64):
+        w = workloads.small(1, H, [n], seed=n + H, device=dev)
+        _check_full(w, "B=1 n=%d H=%d" % (n, H))
