@@ -1,32 +1,45 @@
-// Split-K MLA decode over a paged FP8-E4M3FN latent cache for high head
-// counts (64 or more query heads per KV head), for gfx950.
+// Split-K MLA decode and extend over a paged FP8-E4M3FN latent cache for
+// high head counts (64 query heads per workgroup), for gfx950, with the
+// workgroup's waves specialised by role.
 //
 // Same computation, work split, partial format and combine as the 16-head
-// kernel (mla_decode.hip); what changes is the work inside a workgroup.  With
-// 16 heads per workgroup, H = 128 needs eight workgroups per segment, each of
-// which copies every tile and pays the per-tile latencies for one 16-head
-// slice of the math.  Here one workgroup (8 waves) takes 64 heads (four
-// groups of 16) over 64-token tiles, so a tile is copied and exchanged once
-// per 64 heads and each wave issues four times the MFMA work per tile:
-//  * wave w owns head group w & 3 (its 16 heads' query in registers) and
-//    tokens [32(w >> 2), +32) of the tile for the score product
-//    S^T = K q^T (MFMA 16x16x32 bf16, two 16-token blocks);
-//  * the two waves of a head group exchange maxima and probabilities
-//    through LDS;
-//  * for P.V, wave w owns output columns [256(w >> 2), +256) of its head
-//    group: O^T = V^T P^T over all 64 tokens (16 column blocks of 16, MFMA
-//    16x16x32 f16 on FP16 probabilities), with the transposed FP8 value
-//    operand read by ds_read_b64_tr_b8.
-// Rows are copied global -> LDS (global_load_lds) into three slots of 64
-// rows: tile k+2 goes into the slot of tile k-1 once every wave has finished
-// tile k-1's value reads (the first barrier of tile k), ~1.5 tiles ahead.
+// kernel (mla_decode.hip).  With 64 heads per KV row the work per row is
+// dense (2 x 64 x 1088 flops per token against 576 bytes), so the kernel is
+// bound by its matrix and conversion work rather than by HBM.  Two choices
+// follow from that:
+//  * Roles.  Waves 0-3 ("score waves") each own one head group of 16 heads
+//    over the whole tile: S^T = K q^T (MFMA 16x16x32 bf16, K converted from
+//    FP8 in registers, the group's query held in registers), their own online
+//    softmax (every token of the tile belongs to the wave, so no maximum is
+//    exchanged), and FP16 probabilities written to LDS.  Waves 4-7 ("value
+//    waves") each own 128 output columns of all 64 heads: O^T = V^T P^T
+//    (MFMA 16x16x32 f16), each value byte read transposed
+//    (ds_read_b64_tr_b8) and converted once for the four head groups.  A
+//    score wave never holds output accumulators and a value wave never holds
+//    a query, which keeps both within 256 registers at two waves per SIMD,
+//    one of each role, so that one's matrix work can run under the other's
+//    conversions.
+//  * Half-tile pipeline.  Time is cut into half-tile intervals (32 tokens)
+//    separated by one workgroup barrier: in interval h the score waves
+//    produce the probabilities of half-tile h while the value waves consume
+//    those of half-tile h - 1.  The value waves, which have the lighter
+//    share of the arithmetic, also copy the rows global -> LDS (16 rows
+//    each) into four slots of 64 rows, two and a half tiles ahead of use;
+//    the slot ids go through a small LDS ring two tiles ahead of that, so
+//    that no register is ever the destination of a row or id load in flight.
+//    A score wave issues no copies: its only loads are its queries.
 //
-// The extend instantiation (EXT) serves several query tokens per request:
-// the 64 rows of a workgroup are (token, head) pairs of one virtual request
-// (a request and a block of its query tokens, built on the device), so every
-// KV tile is shared by the block's tokens as it is by the heads.  A wave's 16
-// rows belong to one token, whose causal limit masks the scores; a token
-// without visible tokens in a piece yields an empty partial (lse -inf).
+// Every wait is exact: each wave counts the loads it has issued and records
+// the issue index of each operation it will wait for; loads retire in issue
+// order, so "at most (issued - 1 - index) outstanding" proves that operation
+// complete.  Stores are not counted, which can only make a wait stricter.
+//
+// The extend instantiation (EXT) serves several query tokens per request: a
+// workgroup's 64 rows are (token, head) pairs of one virtual request (a
+// request and a block of its query tokens, built on the device), a score
+// wave's 16 rows belong to one token whose causal limit masks its scores,
+// and a token without visible tokens in a piece yields an empty partial
+// (lse -inf).
 #include "decode_host.h"
 
 namespace fp8mla {
@@ -36,19 +49,22 @@ using namespace decode;
 
 constexpr int NWAVES = 8;
 constexpr int THREADS = 64 * NWAVES;              // 512
-constexpr int GROUPS = 4;                         // head groups of 16 per workgroup
+constexpr int GROUPS = 4;                         // head groups of 16: one per score wave
 constexpr int WG_HEADS = GROUPS * HEADS;          // 64
 constexpr int TILE = 64;                          // tokens per tile
 constexpr int TILE_SHIFT = 6;
-constexpr int NSLOTS = 3;
+constexpr int NSLOTS = 4;                         // row slots (tile j in slot j % 4)
 constexpr int ROW_SLOTS = KV_CHUNKS + 1;          // 37 (odd 16-byte stride)
 constexpr int ROWB = 16 * ROW_SLOTS;              // 592
 constexpr int TILE_BYTES = TILE * ROWB;           // 37888
 constexpr int KSTEPS = KV_WIDTH / 64;             // 9
 constexpr int QSTEPS = 2 * KSTEPS;                // 18
-constexpr int ROWS_PER_WAVE = TILE / NWAVES;      // 8 rows copied by each wave
-constexpr int DMA_OPS = (ROWS_PER_WAVE * ROW_SLOTS + 63) / 64;  // 5
-constexpr int VBLOCKS = (V_WIDTH / 2) / 16;       // 16 output blocks per wave
+constexpr int COPIERS = 4;                        // the value waves copy the rows
+constexpr int ROWS_PER_COPIER = TILE / COPIERS;   // 16 rows copied by each value wave
+constexpr int DMA_OPS = (ROWS_PER_COPIER * ROW_SLOTS + 63) / 64;  // 10
+constexpr int VCOLS = V_WIDTH / GROUPS;           // 128 output columns per value wave
+constexpr int VBLOCKS = VCOLS / 16;               // 8 column blocks of 16
+constexpr int ID_SLOTS = 4;                       // slot-id ring entries per wave
 static_assert(TILE == 1 << TILE_SHIFT, "tile size");
 static_assert(TILE == kH64TileTokens, "host and kernel tile sizes agree");
 static_assert(TILE_SHIFT == kExtendTileShift, "extend's tile CSR counts this kernel's tiles");
@@ -89,38 +105,51 @@ __device__ __forceinline__ void pin_q(bf16x8_t (&q)[QSTEPS]) {
                  "+v"(q[15]), "+v"(q[16]), "+v"(q[17]));
 }
 
-// Wait until at most n vector-memory operations are outstanding (n is
-// wave-uniform and one of the counts this pipeline produces; any other value
-// waits for everything).
-__device__ __forceinline__ void wait_vm_upto(int n) {
-  switch (n) {
-    case 1: wait_vm<1>(); break;
-    case 5: wait_vm<5>(); break;
-    case 6: wait_vm<6>(); break;
-    case 19: wait_vm<19>(); break;
-    case 24: wait_vm<24>(); break;
-    default: wait_vm<0>(); break;
-  }
+// Global -> LDS copy of 4 bytes per active lane (lane l's dword lands at
+// lds_base + 4 l).
+__device__ __forceinline__ void issue_lds_dma4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
 }
 
-// Tile row of MFMA row m of 16-token block B.  Odd blocks use row m ^ 12 so
-// that the transposed value reads of two consecutive blocks fall in distinct
-// LDS banks.
-__device__ __forceinline__ int tile_row(int B, int m) { return 16 * B + ((B & 1) ? (m ^ 12) : m); }
+// Wait until at most n (wave-uniform) of this wave's vector-memory operations
+// are outstanding, rounded down to the counts this pipeline produces (a
+// smaller count only waits longer).  n < 0 cannot occur.
+__device__ __forceinline__ void wait_vm_atmost(int n) {
+  n = __builtin_amdgcn_readfirstlane(n);
+  if (n >= 31) wait_vm<31>();
+  else if (n >= 23) wait_vm<23>();
+  else if (n >= 22) wait_vm<22>();
+  else if (n >= 21) wait_vm<21>();
+  else if (n >= 13) wait_vm<13>();
+  else if (n >= 12) wait_vm<12>();
+  else if (n >= 11) wait_vm<11>();
+  else if (n >= 3) wait_vm<3>();
+  else if (n >= 2) wait_vm<2>();
+  else if (n >= 1) wait_vm<1>();
+  else wait_vm<0>();
+  asm volatile("" ::: "memory");  // no LDS read of landed data moves above the wait
+}
 
 template <bool EXT>
 __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSLOTS * TILE_BYTES];
-  __shared__ float mx_lds[NWAVES][HEADS];
-  __shared__ uint2 p_lds[NWAVES][2][64];
-  __shared__ float l_lds[NWAVES][HEADS];
+  // slot ids of a tile's rows, per copying wave: [value wave][ring entry][row]
+  __shared__ int32_t idring[COPIERS][ID_SLOTS][ROWS_PER_COPIER];
+  // probabilities of a half-tile, per head group: [parity][group][block][lane]
+  __shared__ uint2 pbuf[2][GROUPS][2][64];
+  // rescale factor of each head's running sums at a half-tile: [parity][group][head]
+  __shared__ float abuf[2][GROUPS][HEADS];
+  // a finished request's (or piece's) row sums and maxima: [group][head]
+  __shared__ float lfin[GROUPS][HEADS];
+  __shared__ float mfin[GROUPS][HEADS];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = lane & 15;
   const int g = lane >> 4;
-  const int hgl = w & 3;   // head group of this wave
-  const int half = w >> 2;  // token half (scores) and column half (P.V)
 
   // p.HG counts sets of 64 heads here
   int item = blockIdx.x;
@@ -128,298 +157,399 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   if (item >= p.items) return;
   const int seg = item / p.HG;
   const int hs = item - seg * p.HG;
-  // row: this lane's row of the workgroup's partial results; decode: the
-  // head.  Extend: rows are (token tk of the block, head), 16-row groups never
-  // straddle tokens (rows per token is a multiple of 16), so tk is per wave.
-  const int row = hs * WG_HEADS + hgl * HEADS + t;
-  int head = row, tk = 0;
-  if constexpr (EXT) {
-    if (p.rows_per_tok > 0) {
-      tk = (hgl * HEADS) / p.rows_per_tok;
-      head = hgl * HEADS - tk * p.rows_per_tok + t;
-    }
-  }
 
   SegmentSpan span;
   // (extend: the virtual requests' CSR counts tiles already)
   if (!find_segment<EXT ? 0 : TILE_SHIFT, THREADS, WG_HEADS, !EXT>(p, seg, hs, lane, span)) return;
-  const int ntiles = span.ntiles;
+  const int ntiles = __builtin_amdgcn_readfirstlane(span.ntiles);
   using Cursor = TileCursor<TILE_SHIFT, EXT>;
-  Cursor cc;
+  Cursor cc;  // tile being worked on (score waves: scores; value waves: P.V)
   cc.start(p, span, lane);
-  Cursor lc = cc;
 
+  // lane index the compiler cannot see through: per-lane address math is
+  // redone at each use instead of held in registers across the tile loop
   auto opaque_lane = [&]() -> int {
     int l = lane;
     asm volatile("" : "+v"(l));
     return l;
   };
-  // index of the load cursor's tile: lane l (and copies) holds the slot of
-  // row 8w + (l & 7); tokens past the request read the tile's first row
-  auto load_next_index = [&]() -> int32_t {
-    const int tlo = lc.tile_lo();
-    const int tok = tlo + ROWS_PER_WAVE * w + (t & 7);
-    const int32_t* a = lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) : p.indices;
-    const int32_t v = issue_load_i32(a);
-    lc.advance(p, lane);
-    return v;
-  };
-  const uint32_t lds_tiles = (uint32_t)(uintptr_t)(
-      (__attribute__((address_space(3))) uint8_t*)&kv_lds[0]);
-  // rows 8w .. 8w+7 of a tile into a slot: op j fills 16-byte LDS chunks
-  // 64j .. 64j+63 of the wave's block of 8 x 37 (row P / 37, chunk P % 37;
-  // the pad chunk gets a copy of chunk 35; lanes past the block masked off)
-  auto issue_tile = [&](int slot, int32_t idx) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(
-        lds_tiles + (uint32_t)(slot * TILE_BYTES + ROWS_PER_WAVE * w * ROWB));
-    const int ln = opaque_lane();
-#pragma unroll
-    for (int j = 0; j < DMA_OPS; ++j) {
-      const int P = 64 * j + ln;
-      const int r = P / ROW_SLOTS;
-      const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
-      const uint32_t s = (uint32_t)__shfl(idx, r & 7);
-      const uint8_t* a = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
-      if (j < DMA_OPS - 1 || P < ROWS_PER_WAVE * ROW_SLOTS) {
-        // decode reads each row once per head group, close together in time
-        // (non-temporal hint); extend re-reads a request's rows for each of
-        // its query blocks (default policy)
-        if constexpr (!EXT) issue_lds_dma16_nt(a, base + 1024 * j);
-        else issue_lds_dma16(a, base + 1024 * j);
+  // Row tt of head group hg: partial-result row, and (extend) token of the
+  // block and head.
+  auto group_row = [&](int hg, int tt, int& tok, int& hd) {
+    const int r = hs * WG_HEADS + hg * HEADS + tt;
+    tok = 0;
+    hd = r;
+    if constexpr (EXT) {
+      if (p.rows_per_tok > 0) {
+        tok = (hg * HEADS) / p.rows_per_tok;
+        hd = hg * HEADS - tok * p.rows_per_tok + tt;
       }
     }
+    return r;
   };
 
-  // query of this wave's head group, in the d-order of the K reads: step
-  // s = 2i + e, lane (t, g): q[head t][64i + 16g + 8e .. +8]
-  auto q_lane_ptr = [&](const Cursor& c) -> const uint16_t* {
-    int64_t qrow = c.b;
-    if constexpr (EXT) qrow = c.q_row0() + min(tk, c.q_tokens() - 1);
-    return p.q + (qrow * p.H + min(head, p.H - 1)) * KV_WIDTH + 16 * g;
+  // ---- loads and their bookkeeping.  nops counts this wave's loads (a
+  // score wave: query loads; a value wave: row and id copies); a recorded
+  // index i is complete once at most nops - 1 - i loads are outstanding.
+  int nops = 0;
+  auto wait_done = [&](int op) { wait_vm_atmost(nops - 1 - op); };
+  // k loads issued: returns the index of the last (all of it wave-uniform)
+  auto count_ops = [&](int k) -> int {
+    nops = __builtin_amdgcn_readfirstlane(nops + k);
+    return nops - 1;
   };
-  // rows without a query (heads past H; extend: tokens past the block) keep a zero query
-  auto row_idle = [&]() -> bool {
-    if constexpr (EXT) return head >= p.H || tk >= cc.q_tokens();
-    return head >= p.H;
-  };
-  bf16x8_t qr[QSTEPS];
-  auto finish_q = [&]() {
+
+  bool whole_request = span.j0 == 0;
+  int P_cur = span.P0;
+  const int H2 = 2 * ntiles;  // intervals with scores; one more for the last P.V
+
+  if (w < GROUPS) {
+    // ======================= score wave: head group s ======================
+    const int s = w;
+    int tk = 0, head = 0;
+    group_row(s, t, tk, head);
+    // query of head group s, in the d-order of the K reads: step 2i + e,
+    // lane (t, g): q[head t][64i + 16g + 8e .. +8]
+    auto q_ptr = [&](const Cursor& c) -> const uint16_t* {
+      int64_t qrow = c.b;
+      if constexpr (EXT) qrow = c.q_row0() + min(tk, c.q_tokens() - 1);
+      return p.q + (qrow * p.H + min(head, p.H - 1)) * KV_WIDTH + 16 * g;
+    };
+    bf16x8_t qr[QSTEPS];
+    issue_load_q(qr, q_ptr(cc));
+    int q_op = count_ops(QSTEPS);
+    wait_done(q_op);
+    auto row_idle = [&]() -> bool {
+      if constexpr (EXT) return head >= p.H || tk >= cc.q_tokens();
+      return head >= p.H;
+    };
     pin_q(qr);
     if (row_idle()) {
 #pragma unroll
-      for (int s = 0; s < QSTEPS; ++s) qr[s] = bf16x8_t{};
+      for (int i = 0; i < QSTEPS; ++i) qr[i] = bf16x8_t{};
     }
-  };
+    __syncthreads();  // rows of tile 0 published (by the value waves)
 
-  // Prologue: indices of tiles 0 and 1; query, rows of tile 0, index of tile
-  // 2, rows of tile 1.  "At most 6 outstanding" proves query and tile 0.
-  int32_t ixA = load_next_index();  // tile k % 2 == 0: index of tile k + 2
-  int32_t ixB = load_next_index();
-  wait_vm<0>();
-  pin(ixA);
-  pin(ixB);
-  issue_load_q(qr, q_lane_ptr(cc));
-  issue_tile(0, ixA);
-  ixA = load_next_index();
-  if (ntiles > 1) issue_tile(1, ixB);
-  wait_vm_upto(ntiles > 1 ? 1 + DMA_OPS : 1);
-  finish_q();
-  __syncthreads();
-
-  // LDS offsets.  Scores: block B = 2 half + b, lane (t, g) reads chunk 4i + g
-  // of tile row tile_row(B, t).  Values: as in the 16-head kernel with the
-  // wave's column base 256 half.
-  const int k_off0 = tile_row(2 * half, t) * ROWB + 16 * g;
-  const int k_off1 = tile_row(2 * half + 1, t) * ROWB + 16 * g;
-  const int tr_row0 = (t >> 1) < 4 ? 4 * g + (t >> 1) : 16 + 4 * (g ^ 3) + (t >> 1) - 4;
-  const int tr_off = tr_row0 * ROWB + 8 * (t & 1) + 256 * half;
-  const int s_tok0 = 32 * half + 4 * g;             // block 2 half (even)
-  const int s_tok1 = 32 * half + 16 + 4 * (g ^ 3);  // block 2 half + 1 (odd, XOR 12)
-
-  f32x4_t O[VBLOCKS];
-#pragma unroll
-  for (int c = 0; c < VBLOCKS; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_w = 0.f;
-  bool whole_request = span.j0 == 0;
-  int P_cur = span.P0;
-  auto record_pieces = [&]() {
-    if (hs == 0 && threadIdx.x == 0) {
-      const int s0 = span.segment_of(P_cur + START_W);
-      const int s1 = span.segment_of(P_cur + START_W + TILE_W * (cc.nt - 1));
-      p.req_pieces[cc.b] = make_int2(piece_slot(s0, cc.b == span.b0), s1 - s0 + 1);
-    }
-  };
-  if (whole_request) record_pieces();
-
-  auto finish_request = [&](bool complete) {
-    const float lsum = wave_sum_over_groups(l_w);
-    if (g == 0) l_lds[w][t] = lsum;
-    __syncthreads();
-    const float l = l_lds[hgl][t] + l_lds[hgl + 4][t];
-    // lane (t, g) holds columns 256 half + 16c + 4g + 0..3 of its head
-    if (complete) {
-      if (!row_idle()) {
-        int64_t orow = cc.b;
-        if constexpr (EXT) orow = cc.q_row0() + tk;
-        // extend: a token with no visible token gets a zero row
-        const float inv = EXT && l == 0.f ? 0.f : p.kv_scale / l;
-        uint16_t* op = p.out + (orow * p.H + head) * V_WIDTH + 256 * half + 4 * g;
-#pragma unroll
-        for (int c = 0; c < VBLOCKS; ++c)
-          *reinterpret_cast<uint2*>(op + 16 * c) =
-              make_uint2(pack_bf16x2(O[c][0] * inv, O[c][1] * inv), pack_bf16x2(O[c][2] * inv, O[c][3] * inv));
+    auto record_pieces = [&]() {
+      if (hs == 0 && threadIdx.x == 0) {
+        const int s0 = span.segment_of(P_cur + START_W);
+        const int s1 = span.segment_of(P_cur + START_W + TILE_W * (cc.nt - 1));
+        p.req_pieces[cc.b] = make_int2(piece_slot(s0, cc.b == span.b0), s1 - s0 + 1);
       }
-    } else {
-      const int64_t piece = (int64_t)piece_slot(seg, cc.b == span.b0) * p.Hp + row;
-      const bool empty = EXT && l == 0.f;  // extend: no visible token in this piece
-      const float inv = empty ? 0.f : 1.0f / l;
-      uint16_t* op = p.part_o + piece * V_WIDTH + 256 * half + 4 * g;
-#pragma unroll
-      for (int c = 0; c < VBLOCKS; ++c)
-        *reinterpret_cast<uint2*>(op + 16 * c) =
-            make_uint2(pack_f16x2(O[c][0] * inv, O[c][1] * inv), pack_f16x2(O[c][2] * inv, O[c][3] * inv));
-      if (half == 0 && g == 0)
-        p.part_lse[piece] = empty ? -INFINITY : m_run + __builtin_amdgcn_logf(l) - kPScaleLog2;
-    }
-#pragma unroll
-    for (int c = 0; c < VBLOCKS; ++c) O[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    l_w = 0.f;
-    m_run = -INFINITY;
-  };
+    };
+    if (whole_request) record_pieces();
 
-  // Tile k (slot k % 3): scores -> [barrier: maxima] -> index of k+3, the
-  // next request's query if tile k+1 starts one (qr is dead until then),
-  // rows of k+2 into slot (k+2) % 3 -> probabilities -> rows of k+1 landed ->
-  // [barrier: probabilities, tile k+1] -> P.V.
-  bool q_pending = false;
-  int slot_k = 0;  // k % 3
-  auto process_tile = [&](int k, int32_t& ix_cur, int32_t& ix_next) {
-    const int tile_lo = cc.tile_lo();
-    int tile_hi = cc.tile_hi();
-    if constexpr (EXT) {  // this wave's token sees the first lim tokens of the request
-      const int len = cc.hi - cc.lo;
-      const int lim = p.causal ? len - (cc.q_tokens() - 1 - tk) : len;
-      tile_hi = min(tile_hi, cc.lo + max(lim, 0));
-    }
-    const bool last_of_request = cc.j + 1 == cc.nt;
-    const uint8_t* slot = kv_lds + slot_k * TILE_BYTES;
-    const int slot_next2 = slot_k == 0 ? 2 : slot_k - 1;  // (k + 2) % 3
-    if (q_pending) {  // issued before the rows of tile k+1: those may stay in flight
-      wait_vm_upto(k + 1 < ntiles ? DMA_OPS : 0);
-      finish_q();
-      q_pending = false;
-    }
+    // score operand offsets: block b of half-tile h is tile block 2h + b;
+    // lane (t, g) reads chunk 4i + g of its MFMA row t
+    const int k_off0 = t * ROWB + 16 * g;                // even block: row t
+    const int k_off1 = (16 + (t ^ 12)) * ROWB + 16 * g;  // odd block: row 16 + (t ^ 12)
+    const int s_tok0 = 4 * g;                            // tokens of the lane's rows, even block
+    const int s_tok1 = 16 + 4 * (g ^ 3);                 // odd block (XOR 12)
 
-    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, c0 = a0, c1 = a0;
-    const uint8_t* kp0 = slot + k_off0;
-    const uint8_t* kp1 = slot + k_off1;
-#pragma unroll
-    for (int i = 0; i < KSTEPS; ++i) {
-      const u32x4_t kv0 = *reinterpret_cast<const u32x4_t*>(kp0 + 64 * i);
-      const u32x4_t kv1 = *reinterpret_cast<const u32x4_t*>(kp1 + 64 * i);
-      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[0], kv0[1]), qr[2 * i], a0, 0, 0, 0);
-      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[0], kv1[1]), qr[2 * i], c0, 0, 0, 0);
-      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[2], kv0[3]), qr[2 * i + 1], a1, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[2], kv1[3]), qr[2 * i + 1], c1, 0, 0, 0);
-    }
-    float s0[4], s1[4];
-    float lmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s0[r] = tile_lo + s_tok0 + r < tile_hi ? (a0[r] + a1[r]) * p.score_scale : -INFINITY;
-      s1[r] = tile_lo + s_tok1 + r < tile_hi ? (c0[r] + c1[r]) * p.score_scale : -INFINITY;
-      lmax = fmaxf(lmax, fmaxf(s0[r], s1[r]));
-    }
-    lmax = wave_max_over_groups(lmax);
-    if (g == 0) mx_lds[w][t] = lmax;
-    __syncthreads();
+    float m_run = -INFINITY;
+    float l_w = 0.f;
+    bool q_wait = false;  // the next request's query is in flight
 
-    wait_vm_upto(k + 1 < ntiles ? DMA_OPS : 0);  // index of tile k+2 arrived
-    pin(ix_cur);
-    ix_next = load_next_index();
-    const bool new_q = last_of_request && k + 1 < ntiles;
-    Cursor nc = cc;
-    if (new_q) {
-      nc.advance(p, lane);
-      issue_load_q(qr, q_lane_ptr(nc));
-    }
-    if (k + 2 < ntiles) issue_tile(slot_next2, ix_cur);
+    for (int h = 0; h <= H2; ++h) {
+      const int m = h >> 1;
+      if (h < H2) {
+        const int half = h & 1;
+        if (q_wait) {
+          wait_done(q_op);
+          pin_q(qr);
+          if (row_idle()) {
+#pragma unroll
+            for (int i = 0; i < QSTEPS; ++i) qr[i] = bf16x8_t{};
+          }
+          q_wait = false;
+        }
+        const int tile_lo = cc.tile_lo();
+        int tile_hi = cc.tile_hi();
+        if constexpr (EXT) {  // this group's token sees the first lim tokens of the request
+          const int len = cc.hi - cc.lo;
+          const int lim = p.causal ? len - (cc.q_tokens() - 1 - tk) : len;
+          tile_hi = min(tile_hi, cc.lo + max(lim, 0));
+        }
+        const uint8_t* slot = kv_lds + (m & (NSLOTS - 1)) * TILE_BYTES + 32 * ROWB * half;
+        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, c0 = a0, c1 = a0;
+        const uint8_t* kp0 = slot + k_off0;
+        const uint8_t* kp1 = slot + k_off1;
+#pragma unroll
+        for (int i = 0; i < KSTEPS; ++i) {
+          const u32x4_t kv0 = *reinterpret_cast<const u32x4_t*>(kp0 + 64 * i);
+          const u32x4_t kv1 = *reinterpret_cast<const u32x4_t*>(kp1 + 64 * i);
+          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[0], kv0[1]), qr[2 * i], a0, 0, 0, 0);
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[0], kv1[1]), qr[2 * i], c0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[2], kv0[3]), qr[2 * i + 1], a1, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[2], kv1[3]), qr[2 * i + 1], c1, 0, 0, 0);
+        }
+        float s0[4], s1[4];
+        float lmax = -INFINITY;
+        const int hb = tile_lo + 32 * half;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s0[r] = hb + s_tok0 + r < tile_hi ? (a0[r] + a1[r]) * p.score_scale : -INFINITY;
+          s1[r] = hb + s_tok1 + r < tile_hi ? (c0[r] + c1[r]) * p.score_scale : -INFINITY;
+          lmax = fmaxf(lmax, fmaxf(s0[r], s1[r]));
+        }
+        lmax = wave_max_over_groups(lmax);  // over the half-tile's 32 tokens
+        const float m_new = fmaxf(m_run, lmax);
+        // extend: while a token has seen nothing (m -inf), subtract 0 instead
+        const float m_sub = EXT && m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
+        l_w *= alpha;
+        m_run = m_new;
+        float pr0[4], pr1[4];
+        const float m_p = m_sub - kPScaleLog2;  // probabilities scaled by 2^15 (FP16 P.V)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pr0[r] = __builtin_amdgcn_exp2f(s0[r] - m_p);
+          pr1[r] = __builtin_amdgcn_exp2f(s1[r] - m_p);
+        }
+        const uint32_t p01 = pack_f16x2(pr0[0], pr0[1]), p23 = pack_f16x2(pr0[2], pr0[3]);
+        const uint32_t q01 = pack_f16x2(pr1[0], pr1[1]), q23 = pack_f16x2(pr1[2], pr1[3]);
+        l_w += (f16_lo(p01) + f16_hi(p01)) + (f16_lo(p23) + f16_hi(p23)) +
+               (f16_lo(q01) + f16_hi(q01)) + (f16_lo(q23) + f16_hi(q23));
+        pbuf[h & 1][s][0][lane] = make_uint2(p01, p23);
+        pbuf[h & 1][s][1][lane] = make_uint2(q01, q23);
+        if (g == 0) abuf[h & 1][s][t] = alpha;
 
-    const float tmax = fmaxf(mx_lds[hgl][t], mx_lds[hgl + 4][t]);
-    const float m_new = fmaxf(m_run, tmax);
-    // extend: while a token has seen nothing (m -inf), subtract 0 instead
-    const float m_sub = EXT && m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int c = 0; c < VBLOCKS; ++c) O[c] *= alpha;
-      l_w *= alpha;
-    }
-    m_run = m_new;
-    float pr0[4], pr1[4];
-    const float m_p = m_sub - kPScaleLog2;  // probabilities scaled by 2^15 (FP16 P.V)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pr0[r] = __builtin_amdgcn_exp2f(s0[r] - m_p);
-      pr1[r] = __builtin_amdgcn_exp2f(s1[r] - m_p);
-    }
-    const uint32_t p01 = pack_f16x2(pr0[0], pr0[1]), p23 = pack_f16x2(pr0[2], pr0[3]);
-    const uint32_t q01 = pack_f16x2(pr1[0], pr1[1]), q23 = pack_f16x2(pr1[2], pr1[3]);
-    l_w += (f16_lo(p01) + f16_hi(p01)) + (f16_lo(p23) + f16_hi(p23)) +
-           (f16_lo(q01) + f16_hi(q01)) + (f16_lo(q23) + f16_hi(q23));
-    p_lds[w][0][lane] = make_uint2(p01, p23);
-    p_lds[w][1][lane] = make_uint2(q01, q23);
-    // rows of tile k+1 landed (younger: index k+3, maybe a query, rows k+2)
-    if (k + 1 < ntiles) wait_vm_upto(1 + (new_q ? QSTEPS : 0) + (k + 2 < ntiles ? DMA_OPS : 0));
-    __syncthreads();
-
-    // P.V over the tile's 64 tokens: step st covers blocks 2st and 2st+1,
-    // whose probabilities the wave (hgl, st) produced
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const uint2 x = p_lds[hgl + 4 * st][0][lane];
-      const uint2 y = p_lds[hgl + 4 * st][1][lane];
-      const u32x4_t pv = {x.x, x.y, y.x, y.y};
-      const f16x8_t pb = __builtin_bit_cast(f16x8_t, pv);
-      const uint8_t* vb = slot + tr_off + 32 * ROWB * st;
-#pragma unroll
-      for (int c = 0; c < VBLOCKS; ++c) {
-        const i32x2_t vt = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) i32x2_t*)(vb + 16 * c));
-        O[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16x8((uint32_t)vt.x, (uint32_t)vt.y),
-                                                      pb, O[c], 0, 0, 0);
+        if (half == 1) {
+          const bool last_of_request = cc.j + 1 == cc.nt;
+          if (last_of_request || m + 1 == ntiles) {
+            // the request's (or piece's) row sums and maximum, for the value waves
+            const float lsum = wave_sum_over_groups(l_w);
+            if (g == 0) {
+              lfin[s][t] = lsum;
+              mfin[s][t] = m_run;
+            }
+            l_w = 0.f;
+            m_run = -INFINITY;
+          }
+          if (last_of_request && m + 1 < ntiles) {
+            P_cur += TILE_W * cc.nt + START_W;
+            cc.advance(p, lane);
+            whole_request = true;
+            record_pieces();
+            issue_load_q(qr, q_ptr(cc));  // waited for at the start of the next interval
+            q_op = count_ops(QSTEPS);
+            q_wait = true;
+          } else {
+            cc.advance(p, lane);
+          }
+        }
       }
+      __syncthreads();
     }
+  } else {
+    // ======================= value wave: columns 128v .. +127 =================
+    const int v = w - GROUPS;
+    Cursor lc = cc;  // next tile whose slot ids are copied
+    const uint32_t lds_tiles = (uint32_t)(uintptr_t)(
+        (__attribute__((address_space(3))) uint8_t*)&kv_lds[0]);
+    const uint32_t lds_ids = (uint32_t)(uintptr_t)(
+        (__attribute__((address_space(3))) int32_t*)&idring[v][0][0]);
+    // slot ids of the load cursor's tile j: lane r < 16 copies the id of row
+    // 16v + r into ring entry j % 4 (tokens past the request: the tile's
+    // first row; past the segment's last tile: entry 0 of kv_indices, unused)
+    auto copy_ids = [&](int j) -> int {
+      const int ln = opaque_lane();
+      const uint32_t base =
+          __builtin_amdgcn_readfirstlane(lds_ids + 4 * ROWS_PER_COPIER * (j & (ID_SLOTS - 1)));
+      const int tlo = lc.tile_lo();
+      const int tok = tlo + ROWS_PER_COPIER * v + ln;
+      const int32_t* a = lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) : p.indices;
+      if (ln < ROWS_PER_COPIER) issue_lds_dma4(a, base);
+      lc.advance(p, lane);
+      return count_ops(1);
+    };
+    // rows 16v .. 16v+15 of tile j into slot j % 4: op i fills 16-byte LDS
+    // chunks 64i .. 64i+63 of the wave's block of 16 x 37 (row P / 37, chunk
+    // P % 37; the pad chunk gets a copy of chunk 35; lanes past the block
+    // masked off).  Its slot ids must have landed.  Returns the index of its
+    // last op.
+    auto copy_rows = [&](int j) -> int {
+      const uint32_t base = __builtin_amdgcn_readfirstlane(
+          lds_tiles + (uint32_t)((j & (NSLOTS - 1)) * TILE_BYTES + ROWS_PER_COPIER * v * ROWB));
+      const int32_t* ids = &idring[v][j & (ID_SLOTS - 1)][0];
+      const int ln = opaque_lane();
+#pragma unroll
+      for (int i = 0; i < DMA_OPS; ++i) {
+        const int P = 64 * i + ln;
+        const int r = P / ROW_SLOTS;
+        const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
+        const uint32_t s = (uint32_t)ids[r & (ROWS_PER_COPIER - 1)];  // negative ids compare as large
+        const uint8_t* a = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
+        if (i < DMA_OPS - 1 || P < ROWS_PER_COPIER * ROW_SLOTS) {
+          // decode reads each row once per head set, close together in time
+          // (non-temporal hint); extend re-reads a request's rows for each of
+          // its query blocks (default policy)
+          if constexpr (!EXT) issue_lds_dma16_nt(a, base + 1024 * i);
+          else issue_lds_dma16(a, base + 1024 * i);
+        }
+      }
+      return count_ops(DMA_OPS);
+    };
 
-    if (last_of_request || k + 1 == ntiles) finish_request(whole_request && last_of_request);
-    if (new_q) {
-      P_cur += TILE_W * cc.nt + START_W;
-      cc = nc;
-      whole_request = true;
-      record_pieces();
-      q_pending = true;
-    } else {
-      cc.advance(p, lane);
+    // Prologue: slot ids of tiles 0-3; once those of 0-2 have landed, rows of
+    // tiles 0-2, then the ids of tile 4 (ring entry 0: tile 0's ids were read
+    // to address its row copies).  Pipeline state for the first odd interval
+    // (m = 0): rows of tiles m + 1, m + 2 and ids of tiles m + 3, m + 4 in
+    // flight.
+    copy_ids(0);
+    copy_ids(1);
+    const int id2 = copy_ids(2);
+    int id_a = copy_ids(3);  // ids of tile m + 3
+    wait_done(id2);
+    const int r0 = copy_rows(0);
+    int r_m1 = ntiles > 1 ? copy_rows(1) : -1;  // last op of the rows of tile m + 1
+    int r_m2 = ntiles > 2 ? copy_rows(2) : -1;  // ... of tile m + 2
+    int id_b = copy_ids(4);                     // ids of tile m + 4
+    wait_done(r0);
+    __syncthreads();  // rows of tile 0 published
+
+    // Odd interval 2m + 1.  At its start (after the barrier that ends the
+    // last reads of tile m - 1, this role's P.V of its second half) the rows
+    // of tile m + 3 go into tile m - 1's slot and the ids of tile m + 5 into
+    // the ring entry of tile m + 1's; at its end the rows of tile m + 1 (read
+    // from the next interval on) are waited for, and the barrier that ends
+    // the interval publishes them to the score waves.
+    int r_new = -1, id_new = -1;
+    auto issue_copies = [&](int m) {
+      r_new = -1;
+      if (m + 3 < ntiles) {
+        wait_done(id_a);  // ids of tile m + 3
+        r_new = copy_rows(m + 3);
+      }
+      id_new = copy_ids(m + 5);
+    };
+    auto wait_copies = [&]() {
+      wait_done(r_m1);
+      r_m1 = r_m2;
+      r_m2 = r_new;
+      id_a = id_b;
+      id_b = id_new;
+    };
+
+    // transposed value reads: for the 32 tokens of a half-tile, lane i of
+    // group g supplies row 4g + i/2 (i/2 < 4: even block rows 4g..4g+3) or
+    // row 16 + 4(g^3) + i/2 - 4 (odd block rows (4g..4g+3)^12): exactly the
+    // tokens whose probabilities lane (t, g) of a score wave produced
+    auto tr_offset = [&]() -> int {
+      const int ln = opaque_lane();
+      const int tt = ln & 15, gg = ln >> 4;
+      const int row = (tt >> 1) < 4 ? 4 * gg + (tt >> 1) : 16 + 4 * (gg ^ 3) + (tt >> 1) - 4;
+      return row * ROWB + 8 * (tt & 1) + VCOLS * v;
+    };
+
+    f32x4_t O[GROUPS][VBLOCKS];
+#pragma unroll
+    for (int hg = 0; hg < GROUPS; ++hg)
+#pragma unroll
+      for (int c = 0; c < VBLOCKS; ++c) O[hg][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto finish_request = [&](bool complete) {
+      // lane (t, g) holds columns 128v + 16c + 4g + 0..3 of head t of every group
+      const int ln = opaque_lane();
+      const int tt = ln & 15, gg = ln >> 4;
+#pragma unroll
+      for (int hg = 0; hg < GROUPS; ++hg) {
+        const float l = lfin[hg][tt];
+        int tok_g, head_g;
+        const int row_g = group_row(hg, tt, tok_g, head_g);
+        bool idle = head_g >= p.H;
+        if constexpr (EXT) idle = idle || tok_g >= cc.q_tokens();
+        if (complete) {
+          if (!idle) {
+            int64_t orow = cc.b;
+            if constexpr (EXT) orow = cc.q_row0() + tok_g;
+            // extend: a token with no visible token gets a zero row
+            const float inv = EXT && l == 0.f ? 0.f : p.kv_scale / l;
+            uint16_t* op = p.out + (orow * p.H + head_g) * V_WIDTH + VCOLS * v + 4 * gg;
+#pragma unroll
+            for (int c = 0; c < VBLOCKS; ++c)
+              *reinterpret_cast<uint2*>(op + 16 * c) =
+                  make_uint2(pack_bf16x2(O[hg][c][0] * inv, O[hg][c][1] * inv),
+                             pack_bf16x2(O[hg][c][2] * inv, O[hg][c][3] * inv));
+          }
+        } else {
+          const int64_t piece = (int64_t)piece_slot(seg, cc.b == span.b0) * p.Hp + row_g;
+          const bool empty = EXT && l == 0.f;  // extend: no visible token in this piece
+          const float inv = empty ? 0.f : 1.0f / l;
+          uint16_t* op = p.part_o + piece * V_WIDTH + VCOLS * v + 4 * gg;
+#pragma unroll
+          for (int c = 0; c < VBLOCKS; ++c)
+            *reinterpret_cast<uint2*>(op + 16 * c) =
+                make_uint2(pack_f16x2(O[hg][c][0] * inv, O[hg][c][1] * inv),
+                           pack_f16x2(O[hg][c][2] * inv, O[hg][c][3] * inv));
+          if (v == hg && gg == 0)
+            p.part_lse[piece] = empty ? -INFINITY : mfin[hg][tt] + __builtin_amdgcn_logf(l) - kPScaleLog2;
+        }
+      }
+#pragma unroll
+      for (int hg = 0; hg < GROUPS; ++hg)
+#pragma unroll
+        for (int c = 0; c < VBLOCKS; ++c) O[hg][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    };
+
+    for (int h = 0; h <= H2; ++h) {
+      if (h & 1) issue_copies(h >> 1);
+      if (h >= 1) {
+        // P.V of half-tile h - 1: tile pm, half ph
+        const int hp = h - 1;
+        const int pm = hp >> 1, ph = hp & 1;
+        const int ln = opaque_lane();
+        // rescale a head group's sums only where one of its maxima moved
+#pragma unroll
+        for (int hg = 0; hg < GROUPS; ++hg) {
+          const float alpha = abuf[hp & 1][hg][ln & 15];
+          if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+            for (int c = 0; c < VBLOCKS; ++c) O[hg][c] *= alpha;
+          }
+        }
+        f16x8_t pb[GROUPS];
+#pragma unroll
+        for (int hg = 0; hg < GROUPS; ++hg) {
+          const uint2 x = pbuf[hp & 1][hg][0][ln];
+          const uint2 y = pbuf[hp & 1][hg][1][ln];
+          const u32x4_t pv = {x.x, x.y, y.x, y.y};
+          pb[hg] = __builtin_bit_cast(f16x8_t, pv);
+        }
+        // Rows past the request's end in a partial tile are copies of the
+        // tile's first row with probability 0, so their value bytes need no
+        // masking.
+        const uint8_t* vb = kv_lds + (pm & (NSLOTS - 1)) * TILE_BYTES + 32 * ROWB * ph + tr_offset();
+#pragma unroll
+        for (int c = 0; c < VBLOCKS; ++c) {
+          const i32x2_t vt = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (__attribute__((address_space(3))) i32x2_t*)(vb + 16 * c));
+          const f16x8_t va = e4m3x8_to_f16x8((uint32_t)vt.x, (uint32_t)vt.y);
+#pragma unroll
+          for (int hg = 0; hg < GROUPS; ++hg)
+            O[hg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[hg], O[hg][c], 0, 0, 0);
+        }
+        if (ph == 1) {
+          const bool last_of_request = cc.j + 1 == cc.nt;
+          if (last_of_request || pm + 1 == ntiles) finish_request(whole_request && last_of_request);
+          if (last_of_request && pm + 1 < ntiles) whole_request = true;
+          cc.advance(p, lane);
+        }
+      }
+      if (h & 1) wait_copies();
+      __syncthreads();
     }
-    slot_k = slot_k == 2 ? 0 : slot_k + 1;
-  };
-
-  for (int k = 0; k < ntiles; k += 2) {
-    process_tile(k, ixA, ixB);
-    if (k + 1 >= ntiles) break;
-    process_tile(k + 1, ixB, ixA);
   }
-  wait_vm<0>();  // retire index loads issued past the last tile
+  wait_vm<0>();  // retire loads issued past the last tile
 }
 
 }  // namespace
 
 hipError_t launch_mla_decode_h64(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
-                                 const int32_t* kv_indptr, const int32_t* kv_indices,
-                                 int64_t total_tokens, int32_t batch, int32_t num_heads,
-                                 float scale, float sm_scale, uint16_t* out, void* workspace,
-                                 const DecodePlan& pl, hipStream_t stream) {
+                                const int32_t* kv_indptr, const int32_t* kv_indices,
+                                int64_t total_tokens, int32_t batch, int32_t num_heads,
+                                float scale, float sm_scale, uint16_t* out, void* workspace,
+                                const DecodePlan& pl, hipStream_t stream) {
   const decode::SplitParams sp = make_split_params(q, kv_pool, num_slots, kv_indptr, kv_indices,
                                                    total_tokens, batch, num_heads, scale,
                                                    sm_scale, out, workspace, pl);
