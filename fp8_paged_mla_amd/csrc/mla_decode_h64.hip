@@ -373,12 +373,18 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
           lds_tiles + (uint32_t)((j & (NSLOTS - 1)) * TILE_BYTES + ROWS_PER_COPIER * v * ROWB));
       const int32_t* ids = &idring[v][j & (ID_SLOTS - 1)][0];
       const int ln = opaque_lane();
+      // every op's slot id first, so that the LDS reads overlap (a copy's
+      // asm clobbers memory: no read can move past it)
+      uint32_t sid[DMA_OPS];
+#pragma unroll
+      for (int i = 0; i < DMA_OPS; ++i)
+        sid[i] = (uint32_t)ids[((64 * i + ln) / ROW_SLOTS) & (ROWS_PER_COPIER - 1)];
 #pragma unroll
       for (int i = 0; i < DMA_OPS; ++i) {
         const int P = 64 * i + ln;
         const int r = P / ROW_SLOTS;
         const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
-        const uint32_t s = (uint32_t)ids[r & (ROWS_PER_COPIER - 1)];  // negative ids compare as large
+        const uint32_t s = sid[i];  // negative ids compare as large
         const uint8_t* a = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
         if (i < DMA_OPS - 1 || P < ROWS_PER_COPIER * ROW_SLOTS) {
           // decode reads each row once per head set, close together in time
