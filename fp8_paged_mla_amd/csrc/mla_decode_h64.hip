@@ -24,7 +24,7 @@
 //    produce the probabilities of half-tile h while the value waves consume
 //    those of half-tile h - 1.  The value waves, which have the lighter
 //    share of the arithmetic, also copy the rows global -> LDS (16 rows
-//    each) into four slots of 64 rows, two and a half tiles ahead of use;
+//    each) into three slots of 64 rows, one and a half tiles ahead of use;
 //    the slot ids go through a small LDS ring two tiles ahead of that, so
 //    that no register is ever the destination of a row or id load in flight.
 //    A score wave issues no copies: its only loads are its queries.
@@ -53,7 +53,7 @@ constexpr int GROUPS = 4;                         // head groups of 16: one per 
 constexpr int WG_HEADS = GROUPS * HEADS;          // 64
 constexpr int TILE = 64;                          // tokens per tile
 constexpr int TILE_SHIFT = 6;
-constexpr int NSLOTS = 4;                         // row slots (tile j in slot j % 4)
+constexpr int NSLOTS = 3;                         // row slots (tile j in slot j % 3)
 constexpr int ROW_SLOTS = KV_CHUNKS + 1;          // 37 (odd 16-byte stride)
 constexpr int ROWB = 16 * ROW_SLOTS;              // 592
 constexpr int TILE_BYTES = TILE * ROWB;           // 37888
@@ -64,7 +64,7 @@ constexpr int ROWS_PER_COPIER = TILE / COPIERS;   // 16 rows copied by each valu
 constexpr int DMA_OPS = (ROWS_PER_COPIER * ROW_SLOTS + 63) / 64;  // 10
 constexpr int VCOLS = V_WIDTH / GROUPS;           // 128 output columns per value wave
 constexpr int VBLOCKS = VCOLS / 16;               // 8 column blocks of 16
-constexpr int ID_SLOTS = 4;                       // slot-id ring entries per wave
+constexpr int ID_SLOTS = 4;                       // slot-id ring entries per copying wave
 static_assert(TILE == 1 << TILE_SHIFT, "tile size");
 static_assert(TILE == kH64TileTokens, "host and kernel tile sizes agree");
 static_assert(TILE_SHIFT == kExtendTileShift, "extend's tile CSR counts this kernel's tiles");
@@ -120,13 +120,10 @@ __device__ __forceinline__ void issue_lds_dma4(const void* g, uint32_t lds_base)
 __device__ __forceinline__ void wait_vm_atmost(int n) {
   n = __builtin_amdgcn_readfirstlane(n);
   if (n >= 31) wait_vm<31>();
-  else if (n >= 23) wait_vm<23>();
-  else if (n >= 22) wait_vm<22>();
   else if (n >= 21) wait_vm<21>();
-  else if (n >= 13) wait_vm<13>();
   else if (n >= 12) wait_vm<12>();
   else if (n >= 11) wait_vm<11>();
-  else if (n >= 3) wait_vm<3>();
+  else if (n >= 10) wait_vm<10>();
   else if (n >= 2) wait_vm<2>();
   else if (n >= 1) wait_vm<1>();
   else wait_vm<0>();
@@ -270,7 +267,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
           const int lim = p.causal ? len - (cc.q_tokens() - 1 - tk) : len;
           tile_hi = min(tile_hi, cc.lo + max(lim, 0));
         }
-        const uint8_t* slot = kv_lds + (m & (NSLOTS - 1)) * TILE_BYTES + 32 * ROWB * half;
+        const uint8_t* slot = kv_lds + (m % NSLOTS) * TILE_BYTES + 32 * ROWB * half;
         f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, c0 = a0, c1 = a0;
         const uint8_t* kp0 = slot + k_off0;
         const uint8_t* kp1 = slot + k_off1;
@@ -363,14 +360,14 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       lc.advance(p, lane);
       return count_ops(1);
     };
-    // rows 16v .. 16v+15 of tile j into slot j % 4: op i fills 16-byte LDS
+    // rows 16v .. 16v+15 of tile j into slot j % 3: op i fills 16-byte LDS
     // chunks 64i .. 64i+63 of the wave's block of 16 x 37 (row P / 37, chunk
     // P % 37; the pad chunk gets a copy of chunk 35; lanes past the block
     // masked off).  Its slot ids must have landed.  Returns the index of its
     // last op.
     auto copy_rows = [&](int j) -> int {
       const uint32_t base = __builtin_amdgcn_readfirstlane(
-          lds_tiles + (uint32_t)((j & (NSLOTS - 1)) * TILE_BYTES + ROWS_PER_COPIER * v * ROWB));
+          lds_tiles + (uint32_t)((j % NSLOTS) * TILE_BYTES + ROWS_PER_COPIER * v * ROWB));
       const int32_t* ids = &idring[v][j & (ID_SLOTS - 1)][0];
       const int ln = opaque_lane();
       // every op's slot id first, so that the LDS reads overlap (a copy's
@@ -397,42 +394,37 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       return count_ops(DMA_OPS);
     };
 
-    // Prologue: slot ids of tiles 0-3; once those of 0-2 have landed, rows of
-    // tiles 0-2, then the ids of tile 4 (ring entry 0: tile 0's ids were read
-    // to address its row copies).  Pipeline state for the first odd interval
-    // (m = 0): rows of tiles m + 1, m + 2 and ids of tiles m + 3, m + 4 in
-    // flight.
+    // Prologue: slot ids of tiles 0-3; once those of 0 and 1 have landed,
+    // rows of tiles 0 and 1.  Pipeline state for the first odd interval
+    // (m = 0): rows of tile m + 1 and ids of tiles m + 2, m + 3 in flight.
     copy_ids(0);
-    copy_ids(1);
-    const int id2 = copy_ids(2);
-    int id_a = copy_ids(3);  // ids of tile m + 3
-    wait_done(id2);
+    const int id1 = copy_ids(1);
+    int id_a = copy_ids(2);  // ids of tile m + 2
+    int id_b = copy_ids(3);  // ids of tile m + 3
+    wait_done(id1);
     const int r0 = copy_rows(0);
     int r_m1 = ntiles > 1 ? copy_rows(1) : -1;  // last op of the rows of tile m + 1
-    int r_m2 = ntiles > 2 ? copy_rows(2) : -1;  // ... of tile m + 2
-    int id_b = copy_ids(4);                     // ids of tile m + 4
     wait_done(r0);
     __syncthreads();  // rows of tile 0 published
 
     // Odd interval 2m + 1.  At its start (after the barrier that ends the
     // last reads of tile m - 1, this role's P.V of its second half) the rows
-    // of tile m + 3 go into tile m - 1's slot and the ids of tile m + 5 into
-    // the ring entry of tile m + 1's; at its end the rows of tile m + 1 (read
+    // of tile m + 2 go into tile m - 1's slot and the ids of tile m + 4 into
+    // the ring entry of tile m's; at its end the rows of tile m + 1 (read
     // from the next interval on) are waited for, and the barrier that ends
     // the interval publishes them to the score waves.
     int r_new = -1, id_new = -1;
     auto issue_copies = [&](int m) {
       r_new = -1;
-      if (m + 3 < ntiles) {
-        wait_done(id_a);  // ids of tile m + 3
-        r_new = copy_rows(m + 3);
+      if (m + 2 < ntiles) {
+        wait_done(id_a);  // ids of tile m + 2
+        r_new = copy_rows(m + 2);
       }
-      id_new = copy_ids(m + 5);
+      id_new = copy_ids(m + 4);
     };
     auto wait_copies = [&]() {
       wait_done(r_m1);
-      r_m1 = r_m2;
-      r_m2 = r_new;
+      r_m1 = r_new;
       id_a = id_b;
       id_b = id_new;
     };
@@ -525,16 +517,24 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
         // Rows past the request's end in a partial tile are copies of the
         // tile's first row with probability 0, so their value bytes need no
         // masking.
-        const uint8_t* vb = kv_lds + (pm & (NSLOTS - 1)) * TILE_BYTES + 32 * ROWB * ph + tr_offset();
+        const uint8_t* vb = kv_lds + (pm % NSLOTS) * TILE_BYTES + 32 * ROWB * ph + tr_offset();
+        // all of the half-tile's transposed reads, then all conversions, then
+        // the 32 MFMAs back to back
+        i32x2_t vt[VBLOCKS];
 #pragma unroll
-        for (int c = 0; c < VBLOCKS; ++c) {
-          const i32x2_t vt = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        for (int c = 0; c < VBLOCKS; ++c)
+          vt[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
               (__attribute__((address_space(3))) i32x2_t*)(vb + 16 * c));
-          const f16x8_t va = e4m3x8_to_f16x8((uint32_t)vt.x, (uint32_t)vt.y);
+        __builtin_amdgcn_sched_barrier(0);
+        f16x8_t va[VBLOCKS];
+#pragma unroll
+        for (int c = 0; c < VBLOCKS; ++c) va[c] = e4m3x8_to_f16x8((uint32_t)vt[c].x, (uint32_t)vt[c].y);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < VBLOCKS; ++c)
 #pragma unroll
           for (int hg = 0; hg < GROUPS; ++hg)
-            O[hg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[hg], O[hg][c], 0, 0, 0);
-        }
+            O[hg][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[c], pb[hg], O[hg][c], 0, 0, 0);
         if (ph == 1) {
           const bool last_of_request = cc.j + 1 == cc.nt;
           if (last_of_request || pm + 1 == ntiles) finish_request(whole_request && last_of_request);

@@ -4,7 +4,7 @@
 The kernel's time is cut into half-tile intervals, each ended by one
 workgroup barrier.  Score waves compute the scores of half-tile h in interval
 h, value waves the P.V of half-tile h - 1.  The value waves also copy the
-rows of each tile (global -> LDS, a quarter each) into slot tile % 4 and the
+rows of each tile (global -> LDS, a quarter each) into slot tile % 3 and the
 slot ids of each tile into their own LDS ring entry tile % 4; score waves
 only load a query per request.  A wave waits with "at most N of my loads
 outstanding"; loads retire in issue order, so such a wait proves every load
@@ -31,7 +31,7 @@ SRC = os.path.join(ROOT, "fp8_paged_mla_amd", "csrc", "mla_decode_h64.hip")
 
 DMA_OPS = 10       # row-copy ops per value wave per tile (16 rows x 37 chunks of 16 B)
 QSTEPS = 18        # query loads per request (score waves)
-NSLOTS = 4
+NSLOTS = 3
 ID_SLOTS = 4
 
 
@@ -93,28 +93,26 @@ def simulate(T, ends, imm):
     events = []
     for j in range(4):
         v.issue("ids", j)
-    v.wait_done(len(v.ops) - 2)  # ids of tile 2 (tile 3's ids younger)
-    assert all(v.done("ids", j) for j in range(3))
-    for j in range(3):
+    v.wait_done(len(v.ops) - 3)  # ids of tile 1 (those of tiles 2, 3 younger)
+    assert all(v.done("ids", j) for j in range(2))
+    for j in range(2):
         if j < T:
             events.append((-1, "ring_read", j))
             v.issue("rows", j, DMA_OPS)
             events.append((-1, "copy", j))
-    events.append((-1, "ring_write", 4))  # ids of tile 4 into ring entry 0
-    v.issue("ids", 4)
     v.wait_done([i for i, o in enumerate(v.ops) if o == ("rows", 0)][-1])
     events.append((-1, "proven", [j for j in range(T) if v.done("rows", j)]))
     for h in range(2 * T + 1):
         m = h >> 1
         if h & 1:  # start of an odd interval: the copies
-            if m + 3 < T:
-                v.wait_done([i for i, o in enumerate(v.ops) if o == ("ids", m + 3)][-1])
-                assert v.done("ids", m + 3)
-                events.append((h, "ring_read", m + 3))
-                v.issue("rows", m + 3, DMA_OPS)
-                events.append((h, "copy", m + 3))
-            events.append((h, "ring_write", m + 5))
-            v.issue("ids", m + 5)
+            if m + 2 < T:
+                v.wait_done([i for i, o in enumerate(v.ops) if o == ("ids", m + 2)][-1])
+                assert v.done("ids", m + 2)
+                events.append((h, "ring_read", m + 2))
+                v.issue("rows", m + 2, DMA_OPS)
+                events.append((h, "copy", m + 2))
+            events.append((h, "ring_write", m + 4))
+            v.issue("ids", m + 4)
         if h >= 1:
             events.append((h, "read", (h - 1) >> 1))
         if h & 1:  # end of an odd interval: the wait
@@ -184,13 +182,13 @@ def test_wait_counts_are_exact_immediates():
 
 def test_source_matches_model():
     src = open(SRC).read()
-    assert "constexpr int NSLOTS = 4;" in src
+    assert "constexpr int NSLOTS = 3;" in src
     assert "constexpr int ID_SLOTS = 4;" in src
     assert "constexpr int DMA_OPS = (ROWS_PER_COPIER * ROW_SLOTS + 63) / 64;  // 10" in src
     assert "constexpr int ROWS_PER_COPIER = TILE / COPIERS;   // 16" in src
     assert "constexpr int QSTEPS = 2 * KSTEPS;                // 18" in src
-    for expr in ("if (m + 3 < ntiles) {\n        wait_done(id_a);  // ids of tile m + 3\n        r_new = copy_rows(m + 3);",
-                 "id_new = copy_ids(m + 5);\n    };",
+    for expr in ("if (m + 2 < ntiles) {\n        wait_done(id_a);  // ids of tile m + 2\n        r_new = copy_rows(m + 2);",
+                 "id_new = copy_ids(m + 4);\n    };",
                  "if (h & 1) issue_copies(h >> 1);\n      if (h >= 1) {",
                  "if (h & 1) wait_copies();\n      __syncthreads();",
                  "int q_op = count_ops(QSTEPS);\n    wait_done(q_op);",
