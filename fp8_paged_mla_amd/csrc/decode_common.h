@@ -138,8 +138,17 @@ __device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int 
   // The first 64 requests' kv_indptr entries are loaded once, in one memory
   // latency, and serve both passes and the tile cursor's first window: with
   // at most 63 requests no other load precedes the first index load.
-  const int v0 = clamp_tok(p.indptr[min(lane, p.B)], N);
-  const int v1 = clamp_tok(p.indptr[min(lane + 1, p.B)], N);
+  // A decode call with one request needs no load at all: the index contract
+  // (indptr[0] = 0, indptr[batch] = total_tokens) fixes kv_indptr = [0, N],
+  // and skipping it takes one memory latency off the start of small calls.
+  int v0, v1;
+  if (p.B == 1 && p.vinfo == nullptr) {
+    v0 = lane == 0 ? 0 : N;
+    v1 = N;
+  } else {
+    v0 = clamp_tok(p.indptr[min(lane, p.B)], N);
+    v1 = clamp_tok(p.indptr[min(lane + 1, p.B)], N);
+  }
   const int nt0 = lane < p.B ? tiles_between<SHIFT>(v0, v1) : 0;
   sp.win0 = v0;
   int W = 0;
