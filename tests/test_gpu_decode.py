@@ -97,6 +97,20 @@ def test_high_head_counts(dev, H, shape):
     print("H=%d %s tokens=%d" % (H, shape, sum(lengths)), e)
 
 
+def test_high_head_counts_half_tile_edges(dev):
+    """The 64-head kernel works in half-tiles of 32 tokens: requests that end
+    inside, at or just past a half-tile or tile boundary (so that a tile's
+    second half is empty or a request switch follows its first half),
+    hundreds of query switches, at two head sets."""
+    H = 128
+    pattern = [1, 31, 32, 33, 63, 64, 65, 96, 127, 128, 129, 0]
+    need = _h64_tokens(H)
+    lengths = pattern * (need // sum(pattern) + 1)
+    w = workloads.small(len(lengths), H, lengths, seed=31, device=dev)
+    e = _check_full(w, "H=%d half-tile edges" % H)
+    print("H=%d requests=%d tokens=%d" % (H, len(lengths), sum(lengths)), e)
+
+
 def test_all_requests_empty(dev):
     w = workloads.small(4, 16, [0, 0, 0, 0], num_slots=64, device=dev)
     out = _run(w)
