@@ -108,6 +108,18 @@ def read_traffic(launch_units):
         return None
 
 
+def decode_kernel_name(w, dev):
+    """The split kernel the library plans for this workload: 64 heads per
+    workgroup at H >= 64 when there are at least 4 x CUs / ceil(H / 64)
+    64-token tiles, else 16 heads per workgroup."""
+    import torch
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    tiles = (w.total_tokens + 63) // 64
+    if w.H >= 64 and tiles >= 4 * cus // ((w.H + 63) // 64):
+        return "mla_split_h64_kernel<false>"
+    return "mla_split_kernel<%s>" % ("true" if w.H <= 16 else "false")
+
+
 def algorithmic_decode_bytes(w):
     """Bytes a decode call must move: every attended token's 576-byte row and
     4-byte slot id, the indptr entries, q (576 BF16 per head) and out (512
@@ -283,8 +295,9 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": read_traffic(1),
-            "kernel": "one mla_decode_fp8 call: mla_split_kernel + mla_combine_kernel",
+            # counters are committed for the batch-40 workload only
+            "traffic": read_traffic(1) if args.config == 2 else None,
+            "kernel": "one mla_decode_fp8 call: %s + mla_combine_kernel" % decode_kernel_name(base, dev),
             "algorithmic_bytes_per_call": int(mean_algo),
             "algorithmic_bytes": "576 B KV + 4 B index per token, 4 B per indptr entry, "
                                  "2 B per q (576) and out (512) element",
