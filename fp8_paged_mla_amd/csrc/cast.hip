@@ -141,8 +141,10 @@ constexpr int GATHER_STORES = GATHER_ROWS * KV_WIDTH * 2 / 1024;  // 18 stores o
 constexpr int GATHER_ID_SLOTS = GATHER_SLOTS + 2;
 static_assert(GATHER_ROWS * KV_WIDTH == GATHER_OPS * 1024, "chunk is whole 1 KB copy ops");
 
+// 4-byte global -> LDS copy (lane l's dword at lds_base + 4 l), with the wait
+// state an LDS DMA needs after an M0 write.
 __device__ __forceinline__ void issue_lds_dma4(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :
                : "v"(g), "s"(lds_base)
                : "memory", "m0");

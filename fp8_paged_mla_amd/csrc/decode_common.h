@@ -308,9 +308,11 @@ __device__ __forceinline__ int32_t issue_load_i32(const int32_t* p) {
 // Global -> LDS copy of 16 bytes per lane: lane l's bytes land at LDS byte
 // address lds_base + 16*l (lds_base wave-uniform, passed in M0); lanes
 // outside exec write nothing.  The caller waits with vmcnt.  M0 is not
-// otherwise used by these kernels.
+// otherwise used by these kernels; an LDS DMA reading M0 right after an SALU
+// write of it needs one wait state (the s_nop), which the compiler cannot
+// insert into inline assembly itself.
 __device__ __forceinline__ void issue_lds_dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(g), "s"(lds_base)
                : "memory", "m0");
@@ -321,7 +323,7 @@ __device__ __forceinline__ void issue_lds_dma16(const void* g, uint32_t lds_base
 // decode's rows (one head group per segment) 1% faster than with the default
 // policy; the full-pool cast's input 1% slower.
 __device__ __forceinline__ void issue_lds_dma16_nt(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
                : "v"(g), "s"(lds_base)
                : "memory", "m0");

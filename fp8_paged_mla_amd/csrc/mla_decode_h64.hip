@@ -106,9 +106,9 @@ __device__ __forceinline__ void pin_q(bf16x8_t (&q)[QSTEPS]) {
 }
 
 // Global -> LDS copy of 4 bytes per active lane (lane l's dword lands at
-// lds_base + 4 l).
+// lds_base + 4 l), with the wait state an LDS DMA needs after an M0 write.
 __device__ __forceinline__ void issue_lds_dma4(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
                :
                : "v"(g), "s"(lds_base)
                : "memory", "m0");
