@@ -114,6 +114,15 @@ __device__ __forceinline__ void issue_lds_dma4(const void* g, uint32_t lds_base)
                : "memory", "m0");
 }
 
+// max(a, b, c) in one instruction.  (fmaxf on values merged from two paths
+// gets each operand canonicalised first, one more instruction per operand;
+// arithmetic results need none.)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Wait until at most n (wave-uniform) of this wave's vector-memory operations
 // are outstanding, rounded down to the counts this pipeline produces (a
 // smaller count only waits longer).  n < 0 cannot occur.
@@ -137,8 +146,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   __shared__ int32_t idring[COPIERS][ID_SLOTS][ROWS_PER_COPIER];
   // probabilities of a half-tile, per head group: [parity][group][block][lane]
   __shared__ uint2 pbuf[2][GROUPS][2][64];
-  // rescale factor of each head's running sums at a half-tile: [parity][group][head]
-  __shared__ float abuf[2][GROUPS][HEADS];
+  // rescale factor of each head's running sums at a half-tile: [parity][head][group]
+  __shared__ __attribute__((aligned(16))) float abuf[2][HEADS][GROUPS];
   // a finished request's (or piece's) row sums and maxima: [group][head]
   __shared__ float lfin[GROUPS][HEADS];
   __shared__ float mfin[GROUPS][HEADS];
@@ -277,18 +286,25 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
           const u32x4_t kv1 = *reinterpret_cast<const u32x4_t*>(kp1 + 64 * i);
           a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[0], kv0[1]), qr[2 * i], a0, 0, 0, 0);
           c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[0], kv1[1]), qr[2 * i], c0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[2], kv0[3]), qr[2 * i + 1], a1, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[2], kv1[3]), qr[2 * i + 1], c1, 0, 0, 0);
+          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[2], kv0[3]), qr[2 * i + 1], a0, 0, 0, 0);
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[2], kv1[3]), qr[2 * i + 1], c0, 0, 0, 0);
         }
         float s0[4], s1[4];
-        float lmax = -INFINITY;
         const int hb = tile_lo + 32 * half;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          s0[r] = hb + s_tok0 + r < tile_hi ? (a0[r] + a1[r]) * p.score_scale : -INFINITY;
-          s1[r] = hb + s_tok1 + r < tile_hi ? (c0[r] + c1[r]) * p.score_scale : -INFINITY;
-          lmax = fmaxf(lmax, fmaxf(s0[r], s1[r]));
+          s0[r] = a0[r] * p.score_scale;
+          s1[r] = c0[r] * p.score_scale;
         }
+        if (hb + 32 > tile_hi) {  // (wave-uniform) tokens past the end of the request or limit
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            s0[r] = hb + s_tok0 + r < tile_hi ? s0[r] : -INFINITY;
+            s1[r] = hb + s_tok1 + r < tile_hi ? s1[r] : -INFINITY;
+          }
+        }
+        float lmax = max3f(max3f(s0[0], s0[1], s0[2]), max3f(s0[3], s1[0], s1[1]),
+                           max3f(s1[2], s1[3], -INFINITY));
         lmax = wave_max_over_groups(lmax);  // over the half-tile's 32 tokens
         const float m_new = fmaxf(m_run, lmax);
         // extend: while a token has seen nothing (m -inf), subtract 0 instead
@@ -305,11 +321,15 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
         }
         const uint32_t p01 = pack_f16x2(pr0[0], pr0[1]), p23 = pack_f16x2(pr0[2], pr0[3]);
         const uint32_t q01 = pack_f16x2(pr1[0], pr1[1]), q23 = pack_f16x2(pr1[2], pr1[3]);
-        l_w += (f16_lo(p01) + f16_hi(p01)) + (f16_lo(p23) + f16_hi(p23)) +
-               (f16_lo(q01) + f16_hi(q01)) + (f16_lo(q23) + f16_hi(q23));
+        // the row sums take the probabilities as rounded for P.V
+        const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+        l_w = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p01), one2, l_w, false);
+        l_w = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p23), one2, l_w, false);
+        l_w = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q01), one2, l_w, false);
+        l_w = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, q23), one2, l_w, false);
         pbuf[h & 1][s][0][lane] = make_uint2(p01, p23);
         pbuf[h & 1][s][1][lane] = make_uint2(q01, q23);
-        if (g == 0) abuf[h & 1][s][t] = alpha;
+        if (g == 0) abuf[h & 1][t][s] = alpha;
 
         if (half == 1) {
           const bool last_of_request = cc.j + 1 == cc.nt;
@@ -363,27 +383,38 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
     // rows 16v .. 16v+15 of tile j into slot j % 3: op i fills 16-byte LDS
     // chunks 64i .. 64i+63 of the wave's block of 16 x 37 (row P / 37, chunk
     // P % 37; the pad chunk gets a copy of chunk 35; lanes past the block
-    // masked off).  Its slot ids must have landed.  Returns the index of its
-    // last op.
+    // masked off).  What a lane copies depends on the tile only through the
+    // row's slot id, so the rest is computed once: per op, the byte offset
+    // of the lane's row id in a ring entry and the address of its chunk in
+    // row 0 of the pool (held opaque, so that it stays in registers).
+    uint32_t rof[DMA_OPS];
+    uint64_t cbase[DMA_OPS];
+#pragma unroll
+    for (int i = 0; i < DMA_OPS; ++i) {
+      const int P = 64 * i + lane;
+      const int r = P / ROW_SLOTS;
+      const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
+      rof[i] = 4u * (uint32_t)(r & (ROWS_PER_COPIER - 1));
+      cbase[i] = (uint64_t)(uintptr_t)(p.pool + 16 * c);
+      asm volatile("" : "+v"(rof[i]), "+v"(cbase[i]));
+    }
+    // Its slot ids must have landed.  Returns the index of its last op.
     auto copy_rows = [&](int j) -> int {
       const uint32_t base = __builtin_amdgcn_readfirstlane(
           lds_tiles + (uint32_t)((j % NSLOTS) * TILE_BYTES + ROWS_PER_COPIER * v * ROWB));
-      const int32_t* ids = &idring[v][j & (ID_SLOTS - 1)][0];
-      const int ln = opaque_lane();
+      const uint8_t* ids = reinterpret_cast<const uint8_t*>(&idring[v][j & (ID_SLOTS - 1)][0]);
       // every op's slot id first, so that the LDS reads overlap (a copy's
       // asm clobbers memory: no read can move past it)
       uint32_t sid[DMA_OPS];
 #pragma unroll
-      for (int i = 0; i < DMA_OPS; ++i)
-        sid[i] = (uint32_t)ids[((64 * i + ln) / ROW_SLOTS) & (ROWS_PER_COPIER - 1)];
+      for (int i = 0; i < DMA_OPS; ++i) sid[i] = *reinterpret_cast<const uint32_t*>(ids + rof[i]);
+      const int ln = opaque_lane();
 #pragma unroll
       for (int i = 0; i < DMA_OPS; ++i) {
-        const int P = 64 * i + ln;
-        const int r = P / ROW_SLOTS;
-        const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
         const uint32_t s = sid[i];  // negative ids compare as large
-        const uint8_t* a = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
-        if (i < DMA_OPS - 1 || P < ROWS_PER_COPIER * ROW_SLOTS) {
+        const uint8_t* a = reinterpret_cast<const uint8_t*>(
+            (uintptr_t)(cbase[i] + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH));
+        if (i < DMA_OPS - 1 || ln < ROWS_PER_COPIER * ROW_SLOTS - 64 * (DMA_OPS - 1)) {
           // decode reads each row once per head set, close together in time
           // (non-temporal hint); extend re-reads a request's rows for each of
           // its query blocks (default policy)
@@ -498,12 +529,13 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
         const int pm = hp >> 1, ph = hp & 1;
         const int ln = opaque_lane();
         // rescale a head group's sums only where one of its maxima moved
+        // (the four groups' factors of a head in one read)
+        const f32x4_t alpha = *reinterpret_cast<const f32x4_t*>(&abuf[hp & 1][ln & 15][0]);
 #pragma unroll
         for (int hg = 0; hg < GROUPS; ++hg) {
-          const float alpha = abuf[hp & 1][hg][ln & 15];
-          if (__ballot(alpha != 1.0f)) {
+          if (__ballot(alpha[hg] != 1.0f)) {
 #pragma unroll
-            for (int c = 0; c < VBLOCKS; ++c) O[hg][c] *= alpha;
+            for (int c = 0; c < VBLOCKS; ++c) O[hg][c] *= alpha[hg];
           }
         }
         f16x8_t pb[GROUPS];
