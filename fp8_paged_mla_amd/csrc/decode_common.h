@@ -61,17 +61,56 @@ constexpr int kExtQ0Mask = (1 << kExtQ0Bits) - 1;
 constexpr int kExtTokShift = 23;
 constexpr int kExtTailShift = 25;
 
+// Reductions over the four 16-lane rows of a wave (lanes h, h+16, h+32,
+// h+48 hold the same head) with the cross-row swaps of gfx950: swap32(a, b)
+// gives (a's lanes 0-31 in both halves, b's lanes 32-63 in both halves) when
+// a and b hold the same value, swap16 likewise for rows 0/1 and 2/3, so an
+// elementwise op of the two results combines lanes l and l^32 (l^16) in every
+// lane.  The second operand goes through an opaque copy: given one value
+// twice, the compiler folds the two results into one, which is not what the
+// instruction does.
+struct RowPair {
+  float a, b;
+};
+__device__ __forceinline__ RowPair swap_rows32(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x), v = u;
+  asm volatile("" : "+v"(v));
+  const auto r = __builtin_amdgcn_permlane32_swap(u, v, false, false);
+  return {__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+__device__ __forceinline__ RowPair swap_rows16(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x), v = u;
+  asm volatile("" : "+v"(v));
+  const auto r = __builtin_amdgcn_permlane16_swap(u, v, false, false);
+  return {__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+}
+// max without the canonicalising fmaxf adds to each operand the compiler
+// cannot trace to arithmetic (values loaded, exchanged or merged from two
+// paths): one instruction instead of up to three.  IEEE maxNum otherwise: a
+// NaN operand yields the other operand.
+__device__ __forceinline__ float max_f32(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// max(a, b, c) in one instruction, likewise
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ float wave_max_over_groups(float x) {
-  // lanes h, h+16, h+32, h+48 hold the same head
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const RowPair p = swap_rows32(x);
+  const RowPair q = swap_rows16(max_f32(p.a, p.b));
+  return max_f32(q.a, q.b);
 }
 
 __device__ __forceinline__ float wave_sum_over_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const RowPair p = swap_rows32(x);
+  const RowPair q = swap_rows16(p.a + p.b);
+  return q.a + q.b;
 }
 
 __device__ __forceinline__ int clamp_tok(int v, int n) { return v < 0 ? 0 : (v > n ? n : v); }
@@ -117,6 +156,15 @@ __device__ __forceinline__ int request_tiles(const int32_t* indptr, int b, int B
 // N < 2^31 and B <= 2^24, the batch limit the host enforces; for extend,
 // whose CSR counts tiles (SHIFT 0), W <= 4 N + 6 B with N <= 2^28 tiles and
 // B <= 2^25 virtual requests, the bounds its host checks.)
+// floor(a / b) for 0 <= a < 2^53 and 0 < b < 2^31 by one double division
+// (a 64-bit integer division is a ~100-instruction VALU routine).  a and b
+// are exact doubles and the division is correctly rounded, so the quotient q
+// moves by at most q 2^-53 < 1 / b: never onto or across an integer that q
+// is not already on, which is the whole distance to any other integer.
+__device__ __forceinline__ int div_floor_small(int64_t a, int b) {
+  return (int)__builtin_floor((double)a / (double)b);
+}
+
 struct SegmentSpan {
   int nseg;    // segments in use
   int W;       // total weight
@@ -124,7 +172,9 @@ struct SegmentSpan {
   int b0, j0;  // request and tile of its first tile
   int P0;      // weight of the requests before b0
   int win0;    // per lane: clamp(kv_indptr[min(lane, B)]), the first 64-entry window
-  __device__ __forceinline__ int segment_of(int x) const { return (int)((int64_t)x * nseg / W); }
+  __device__ __forceinline__ int segment_of(int x) const {
+    return div_floor_small((int64_t)x * nseg, W);  // x < 2^31, nseg <= CUs: below 2^53
+  }
 };
 
 // One workgroup's segment, found with two wave-wide scans over the requests
@@ -171,8 +221,8 @@ __device__ __forceinline__ bool find_segment(const SplitParams& p, int seg, int 
   }
   const int nseg = min(p.nseg, W / (TILE_W + START_W));
   if (seg >= nseg) return false;
-  const int x_lo = (int)(((int64_t)seg * W + nseg - 1) / nseg);
-  const int x_hi = (int)(((int64_t)(seg + 1) * W + nseg - 1) / nseg);
+  const int x_lo = div_floor_small((int64_t)seg * W + nseg - 1, nseg);  // ceil(seg W / nseg)
+  const int x_hi = div_floor_small((int64_t)(seg + 1) * W + nseg - 1, nseg);
   // global index t0 of the first tile at or after x_lo (its request b0, tile
   // j0, weight P0 before b0) and t1 of the first at or after x_hi
   int t0 = -1, t1 = -1, b0 = 0, j0 = 0, P0 = 0;

@@ -132,18 +132,35 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
   };
   const uint32_t lds_tiles = (uint32_t)(uintptr_t)(
       (__attribute__((address_space(3))) uint8_t*)&kv_lds[0]);
+  // What a lane copies depends on the tile only through the slot ids, so the
+  // rest is computed once: per op, the permute address of the lane holding
+  // its row's id and the address of its chunk in row 0 of the pool (held
+  // opaque, so that they stay in registers).
+  uint32_t src_lane[DMA_OPS];
+  uint64_t cbase[DMA_OPS];
+#pragma unroll
+  for (int j = 0; j < DMA_OPS; ++j) {
+    const int P = 64 * j + lane;
+    const int r = P / ROW_SLOTS;
+    const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
+    src_lane[j] = 4u * (uint32_t)(r & 15);
+    cbase[j] = (uint64_t)(uintptr_t)(p.pool + 16 * c);
+    asm volatile("" : "+v"(src_lane[j]), "+v"(cbase[j]));
+  }
   auto issue_tile = [&](int k, int32_t idx) {
     const uint32_t base =
         __builtin_amdgcn_readfirstlane(lds_tiles + (uint32_t)((k & 1) * TILE_BYTES + 16 * w * ROWB));
+    uint32_t sid[DMA_OPS];
+#pragma unroll
+    for (int j = 0; j < DMA_OPS; ++j)
+      sid[j] = (uint32_t)__builtin_amdgcn_ds_bpermute((int)src_lane[j], idx);
     const int ln = opaque_lane();
 #pragma unroll
     for (int j = 0; j < DMA_OPS; ++j) {
-      const int P = 64 * j + ln;
-      const int r = P / ROW_SLOTS;
-      const int c = min(P - r * ROW_SLOTS, KV_CHUNKS - 1);
-      const uint32_t s = (uint32_t)__shfl(idx, r & 15);
-      const uint8_t* a = p.pool + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH + 16 * c;
-      if (j < DMA_OPS - 1 || P < 16 * ROW_SLOTS) {
+      const uint32_t s = sid[j];  // negative ids compare as large
+      const uint8_t* a = reinterpret_cast<const uint8_t*>(
+          (uintptr_t)(cbase[j] + (uint64_t)(s < p.max_slot ? s : p.max_slot) * KV_WIDTH));
+      if (j < DMA_OPS - 1 || ln < 16 * ROW_SLOTS - 64 * (DMA_OPS - 1)) {
         if constexpr (NT_ROWS) issue_lds_dma16_nt(a, base + 1024 * j);
         else issue_lds_dma16(a, base + 1024 * j);
       }
@@ -306,14 +323,13 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
               (__attribute__((address_space(3))) i32x2_t*)(vbase + 32 * ROWB * st + 16 * c));
     }
     float s[4];
-    float lmax = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool ok = tile_lo + s_tok0 + r < tile_hi;
-      s[r] = ok ? (a0[r] + a1[r]) * p.score_scale : -INFINITY;
-      lmax = fmaxf(lmax, s[r]);
+    for (int r = 0; r < 4; ++r) s[r] = (a0[r] + a1[r]) * p.score_scale;
+    if (tile_lo + TILE > tile_hi) {  // (wave-uniform) a partial tile: mask tokens past its end
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s[r] = tile_lo + s_tok0 + r < tile_hi ? s[r] : -INFINITY;
     }
-    lmax = wave_max_over_groups(lmax);
+    float lmax = wave_max_over_groups(max3f(max3f(s[0], s[1], s[2]), s[3], -INFINITY));
     if (g == 0) mx_lds[w][t] = lmax;
     __syncthreads();
 
@@ -336,10 +352,11 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     }
     if (rows_now) issue_tile(k + 2, ix_cur);
 
-    float tmax = mx_lds[0][t];
-#pragma unroll
-    for (int v = 1; v < NWAVES; ++v) tmax = fmaxf(tmax, mx_lds[v][t]);
-    const float m_new = fmaxf(m_run, tmax);
+    static_assert(NWAVES == 8, "maximum over the waves' maxima");
+    const float tmax = max3f(max3f(mx_lds[0][t], mx_lds[1][t], mx_lds[2][t]),
+                             max3f(mx_lds[3][t], mx_lds[4][t], mx_lds[5][t]),
+                             max_f32(mx_lds[6][t], mx_lds[7][t]));
+    const float m_new = max_f32(m_run, tmax);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     if (__ballot(alpha != 1.0f)) {
 #pragma unroll
@@ -353,7 +370,10 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(s[r] - m_p);
     const uint32_t p01 = pack_f16x2(pr[0], pr[1]);
     const uint32_t p23 = pack_f16x2(pr[2], pr[3]);
-    l_w += (f16_lo(p01) + f16_hi(p01)) + (f16_lo(p23) + f16_hi(p23));
+    // the row sums take the probabilities as rounded for P.V
+    const f16x2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+    l_w = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p01), one2, l_w, false);
+    l_w = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, p23), one2, l_w, false);
     p_lds[w][lane] = make_uint2(p01, p23);
     // rows of tile k+1 (and a new query) landed; younger: index of k+3 unless
     // a query was copied after it, and rows of k+2 if issued

@@ -114,15 +114,6 @@ __device__ __forceinline__ void issue_lds_dma4(const void* g, uint32_t lds_base)
                : "memory", "m0");
 }
 
-// max(a, b, c) in one instruction.  (fmaxf on values merged from two paths
-// gets each operand canonicalised first, one more instruction per operand;
-// arithmetic results need none.)
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
 // Wait until at most n (wave-uniform) of this wave's vector-memory operations
 // are outstanding, rounded down to the counts this pipeline produces (a
 // smaller count only waits longer).  n < 0 cannot occur.

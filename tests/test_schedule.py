@@ -79,3 +79,22 @@ def test_tiny_and_empty():
     check([0, 0, 5, 0], 256)
     check([1] * 40, 256)
     assert split([0, 0], 256)[3] == 0
+
+
+def test_double_division_is_exact_floor():
+    """The kernels compute floor(a / b) (segment of a weighted position, and
+    a segment's bounds) as floor of one correctly rounded double division,
+    claimed exact for 0 <= a < 2^53, 0 < b < 2^31.  Python floats are IEEE
+    doubles with correctly rounded division: check the claim on random and
+    adversarial operands (a one below, at and one above a multiple of b)."""
+    rng = np.random.default_rng(7)
+    cases = []
+    for _ in range(20000):
+        b = int(rng.integers(1, 2**31))
+        k = int(rng.integers(0, (2**53 - 2) // b))
+        for a in (k * b - 1, k * b, k * b + 1, int(rng.integers(0, 2**53))):
+            if 0 <= a < 2**53:
+                cases.append((a, b))
+    cases += [(2**53 - 1, 1), (2**53 - 1, 2**31 - 1), (2**53 - 2, 3), (0, 5), (2**31 - 1, 2**31 - 1)]
+    for a, b in cases:
+        assert int(float(a) / float(b) // 1) == a // b, (a, b)
