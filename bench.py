@@ -55,6 +55,9 @@ def parse_args():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--layers", type=int, default=78, help="config 3: layers per decode step")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GB")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="bound the decode's split-K segments (mla_decode_fp8_segments); "
+                         "default: the library's own partition")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--serving-step", choices=["bf16", "fp8_cast", "fp8_fused"], default=None,
@@ -220,7 +223,8 @@ def main():
     # path); every call still goes through the C ABI's own checks and
     # launches all of the decode's kernels
     calls = [fm.prepare_mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale,
-                                       out=outs[r], workspace=wss[r], stream=stream)
+                                       out=outs[r], workspace=wss[r], stream=stream,
+                                       segments=args.splits)
              for r, w in enumerate(reps)]
 
     def call(i):
@@ -283,6 +287,8 @@ def main():
             "mean_tokens_per_call": round(sum(w.total_tokens for w in reps) / R, 1),
             "replicas_rotated": R,
             "rotated_footprint_GB": round(R * pool_bytes / 1e9, 3),
+            "split_segments": "library default" if args.splits is None else
+                              "at most %d" % args.splits,
         },
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
         "us_per_call": {"p10": round(float(q[0]), 2), "median": round(float(q[1]), 2),
@@ -295,8 +301,9 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            # counters are committed for the batch-40 workload only
-            "traffic": read_traffic(1) if args.config == 2 else None,
+            # counters are committed for the batch-40 workload (library
+            # partition) only
+            "traffic": read_traffic(1) if args.config == 2 and args.splits is None else None,
             "kernel": "one mla_decode_fp8 call: %s + mla_combine_kernel" % decode_kernel_name(base, dev),
             "algorithmic_bytes_per_call": int(mean_algo),
             "algorithmic_bytes": "576 B KV + 4 B index per token, 4 B per indptr entry, "

@@ -110,6 +110,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.scatter_cast_bf16_fp8.restype = ctypes.c_int
     lib.mla_decode_fp8.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, f32, f32, vp, vp, sz, vp]
     lib.mla_decode_fp8.restype = ctypes.c_int
+    lib.mla_decode_fp8_segments.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, f32, f32, vp, vp,
+                                            sz, i32, vp]
+    lib.mla_decode_fp8_segments.restype = ctypes.c_int
     lib.mla_decode_fp8_noalloc.argtypes = [vp, vp, i64, vp, vp, i64, i32, i32, f32, f32, vp, vp]
     lib.mla_decode_fp8_noalloc.restype = ctypes.c_int
     lib.mla_decode_fp8_workspace_bytes.argtypes = [i32, i32, i64]
@@ -320,11 +323,14 @@ def mla_decode_fp8_workspace_bytes(batch: int, num_heads: int, total_tokens: int
 
 def mla_decode_fp8(q: torch.Tensor, kv_pool: torch.Tensor, kv_indptr: torch.Tensor,
                    kv_indices: torch.Tensor, scale: float, sm_scale: float,
-                   out: torch.Tensor = None, workspace: torch.Tensor = None) -> torch.Tensor:
+                   out: torch.Tensor = None, workspace: torch.Tensor = None,
+                   segments: int = None) -> torch.Tensor:
     """Fused MLA decode reading the FP8 pool directly.
 
     q [B, H, 576] bf16; kv_pool [num_slots, 576] E4M3FN; kv_indptr [B+1] int32;
     kv_indices [kv_indptr[B]] int32 slot ids; returns out [B, H, 512] bf16.
+    ``segments`` bounds the split-K partition (mla_decode_fp8_segments);
+    None keeps the library's own.
     """
     kv_pool = _pool_rows(kv_pool)
     _require(q, "q", torch.bfloat16)
@@ -352,11 +358,19 @@ def mla_decode_fp8(q: torch.Tensor, kv_pool: torch.Tensor, kv_indptr: torch.Tens
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         _require(workspace, "workspace", torch.uint8, dev)
         ws_bytes = workspace.numel()
-        _check(lib.mla_decode_fp8(q.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
-                                  kv_indptr.data_ptr(), kv_indices.data_ptr(), total, B, H,
-                                  float(scale), float(sm_scale), out.data_ptr(),
-                                  workspace.data_ptr(), ws_bytes, _stream_handle(dev)),
-               "mla_decode_fp8")
+        if segments is None:
+            _check(lib.mla_decode_fp8(q.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
+                                      kv_indptr.data_ptr(), kv_indices.data_ptr(), total, B, H,
+                                      float(scale), float(sm_scale), out.data_ptr(),
+                                      workspace.data_ptr(), ws_bytes, _stream_handle(dev)),
+                   "mla_decode_fp8")
+        else:
+            _check(lib.mla_decode_fp8_segments(q.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0],
+                                               kv_indptr.data_ptr(), kv_indices.data_ptr(), total,
+                                               B, H, float(scale), float(sm_scale),
+                                               out.data_ptr(), workspace.data_ptr(), ws_bytes,
+                                               int(segments), _stream_handle(dev)),
+                   "mla_decode_fp8_segments")
     return out
 
 
@@ -419,10 +433,11 @@ class PreparedCall:
 def prepare_mla_decode_fp8(q: torch.Tensor, kv_pool: torch.Tensor, kv_indptr: torch.Tensor,
                            kv_indices: torch.Tensor, scale: float, sm_scale: float,
                            out: torch.Tensor = None, workspace: torch.Tensor = None,
-                           stream=None) -> PreparedCall:
+                           stream=None, segments: int = None) -> PreparedCall:
     """mla_decode_fp8 with its arguments checked and marshalled once; returns
     a callable that enqueues the call (on ``stream``, default the current
-    stream at preparation) and returns ``out``."""
+    stream at preparation) and returns ``out``.  ``segments`` bounds the
+    split-K partition (mla_decode_fp8_segments)."""
     kv_pool = _pool_rows(kv_pool)
     _require(q, "q", torch.bfloat16)
     dev = q.device
@@ -457,8 +472,11 @@ def prepare_mla_decode_fp8(q: torch.Tensor, kv_pool: torch.Tensor, kv_indptr: to
             c.c_int32(B), c.c_int32(H), c.c_float(float(scale)), c.c_float(float(sm_scale)),
             c.c_void_p(out.data_ptr()), c.c_void_p(workspace.data_ptr()),
             c.c_size_t(workspace.numel()), c.c_void_p(handle))
-    return PreparedCall(lib.mla_decode_fp8, args, (q, kv_pool, kv_indptr, kv_indices, out, workspace),
-                        out, "mla_decode_fp8")
+    keep = (q, kv_pool, kv_indptr, kv_indices, out, workspace)
+    if segments is not None:
+        args = args[:-1] + (c.c_int32(int(segments)), args[-1])
+        return PreparedCall(lib.mla_decode_fp8_segments, args, keep, out, "mla_decode_fp8_segments")
+    return PreparedCall(lib.mla_decode_fp8, args, keep, out, "mla_decode_fp8")
 
 
 def mla_decode_bf16_workspace_bytes(batch: int, num_heads: int, total_tokens: int,

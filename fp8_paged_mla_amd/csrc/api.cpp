@@ -296,15 +296,27 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
                    const int32_t* kv_indptr, const int32_t* kv_indices, int64_t total_tokens,
                    int32_t batch, int32_t num_heads, float scale, float sm_scale, uint16_t* out,
                    void* workspace, size_t workspace_bytes, void* stream) {
+  return mla_decode_fp8_segments(q, kv_pool, num_slots, kv_indptr, kv_indices, total_tokens,
+                                 batch, num_heads, scale, sm_scale, out, workspace,
+                                 workspace_bytes, INT32_MAX, stream);
+}
+
+int mla_decode_fp8_segments(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                            const int32_t* kv_indptr, const int32_t* kv_indices,
+                            int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
+                            float sm_scale, uint16_t* out, void* workspace,
+                            size_t workspace_bytes, int32_t num_segments, void* stream) {
   const int st = check_decode_fp8_args(q, kv_pool, num_slots, kv_indptr, kv_indices, total_tokens,
                                        batch, num_heads, scale, sm_scale, out);
   if (st != FP8MLA_OK) return st;
+  if (num_segments < 1) return FP8MLA_ERR_BAD_SHAPE;
   if (total_tokens > 0 && !workspace) return FP8MLA_ERR_NULL_PTR;
   if (total_tokens > 0 && !aligned16(workspace)) return FP8MLA_ERR_MISALIGNED;
   const int cus = current_device_cus();
   if (cus <= 0) return FP8MLA_ERR_HIP;
-  const fp8mla::DecodePlan plan = fp8mla::plan_mla_decode(batch, num_heads, total_tokens, cus,
-                                                          fp8mla::fp8_decode_kernel(num_heads, total_tokens, cus));
+  const fp8mla::DecodePlan plan = fp8mla::plan_mla_decode(
+      batch, num_heads, total_tokens, cus, fp8mla::fp8_decode_kernel(num_heads, total_tokens, cus),
+      num_segments);
   if (total_tokens > 0 && workspace_bytes < plan.workspace_bytes) return FP8MLA_ERR_WORKSPACE;
   if (debug_check(kv_indptr, batch, total_tokens, kv_indices, num_slots, cus, stream) != hipSuccess)
     return FP8MLA_ERR_HIP;

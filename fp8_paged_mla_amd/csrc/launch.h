@@ -47,8 +47,10 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 
+// max_segments > 0 bounds the number of segments (for tests of split
+// invariance and for tuning); the workspace size does not depend on it.
 DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_tokens, int num_cus,
-                           DecodeKernel kernel);
+                           DecodeKernel kernel, int32_t max_segments = 0);
 
 inline DecodeKernel fp8_decode_kernel(int32_t num_heads, int64_t total_tokens, int num_cus) {
   if (num_heads < kH64MinHeads) return DecodeKernel::kFp8;

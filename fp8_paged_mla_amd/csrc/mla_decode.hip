@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const CombineParams p)
 }  // namespace
 
 DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_tokens, int num_cus,
-                           DecodeKernel kernel) {
+                           DecodeKernel kernel, int32_t max_segments) {
   const int tile_tokens = kernel == DecodeKernel::kBf16 ? kBf16TileTokens
                           : kernel == DecodeKernel::kFp8H64 ? kH64TileTokens
                                                             : kFp8TileTokens;
@@ -477,6 +477,7 @@ DecodePlan plan_mla_decode(int32_t batch, int32_t num_heads, int64_t total_token
     const int64_t cap = (decode::TILE_W * t + decode::START_W) / (decode::TILE_W + decode::START_W);
     if (nseg > cap) nseg = cap;
   }
+  if (max_segments > 0 && nseg > max_segments) nseg = max_segments;
   if (nseg < 1) nseg = 1;
   pl.nseg = (int32_t)nseg;
   pl.items = pl.nseg * pl.HG;

@@ -169,6 +169,26 @@ int mla_decode_fp8(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
                    uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_fp8_segments -- mla_decode_fp8 with its split-K partition
+ * bounded: the list of request tiles is cut into at most num_segments
+ * segments (never more than mla_decode_fp8 itself would use, which is one
+ * per compute unit and head group, fewer for small calls).  The operation is
+ * mla_decode_fp8's; the partition is this library's own flash-decoding split
+ * (see there), which the result does not depend on beyond rounding.  For
+ * tests of that invariance and for tuning; num_segments = 1 is an unsplit
+ * decode with no merge kernel.  The workspace mla_decode_fp8_workspace_bytes
+ * returns suffices for every num_segments.
+ *   num_segments >= 1, else FP8MLA_ERR_BAD_SHAPE.
+ * All other arguments, layouts, ownership and status codes as mla_decode_fp8
+ * (which is this call with num_segments = INT32_MAX).
+ */
+int mla_decode_fp8_segments(const uint16_t* q, const uint8_t* kv_pool, int64_t num_slots,
+                            const int32_t* kv_indptr, const int32_t* kv_indices,
+                            int64_t total_tokens, int32_t batch, int32_t num_heads, float scale,
+                            float sm_scale, uint16_t* out, void* workspace,
+                            size_t workspace_bytes, int32_t num_segments, void* stream);
+
+/*
  * Workspace size in bytes for mla_decode_fp8 on the CURRENT device with these
  * sizes (0 when total_tokens == 0: no workspace is needed).  Returns 0 for
  * invalid sizes.  For total_tokens > 0 the size depends only on batch and

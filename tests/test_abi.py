@@ -15,6 +15,9 @@ fm = pytest.importorskip("fp8_paged_mla_amd")
 
 
 def _lib():
+    path = os.environ.get("FP8MLA_TEST_LIB")
+    if path:  # another build of the same ABI (the sanitized one: test_abi_sanitized.py)
+        return fm._bind(ctypes.CDLL(path))
     try:
         return fm.library()
     except RuntimeError as e:  # not built
@@ -157,6 +160,29 @@ def test_mla_decode_validation():
     assert _decode(lib, pool=P8) == ERR_ALIGN
     assert _decode(lib, ws=P8) == ERR_ALIGN
     assert _decode(lib, indptr=P16 + 2) == ERR_ALIGN
+
+
+def test_mla_decode_segments_validation():
+    """The bounded-split call shares mla_decode_fp8's checks and rejects a
+    segment bound below 1 before any device call."""
+    lib = _lib()
+
+    def call(S, **kw):
+        a = dict(q=P16, pool=P16, slots=100, indptr=P16, indices=P16, total=10, B=2, H=16,
+                 scale=1.0, sm=0.07, out=P16, ws=P16, ws_bytes=1 << 20, stream=NULL)
+        a.update(kw)
+        return lib.mla_decode_fp8_segments(a["q"], a["pool"], a["slots"], a["indptr"],
+                                           a["indices"], a["total"], a["B"], a["H"], a["scale"],
+                                           a["sm"], a["out"], a["ws"], a["ws_bytes"], S,
+                                           a["stream"])
+
+    assert call(0) == ERR_SHAPE
+    assert call(-3) == ERR_SHAPE
+    assert call(7, B=0) == ERR_SHAPE
+    assert call(7, scale=0.0) == ERR_SCALAR
+    assert call(7, q=NULL) == ERR_NULL
+    assert call(7, ws=NULL) == ERR_NULL
+    assert call(7, out=P8) == ERR_ALIGN
 
 
 def test_mla_decode_bf16_validation():
@@ -324,7 +350,7 @@ def test_probe_header_symbols_exported_and_validated():
     for n in names:
         assert hasattr(lib, n), n
     from fp8_paged_mla_amd import probe
-    L = probe._lib()
+    L = probe._lib(lib)
     assert L.fp8mla_probe_read(P16, 0, 256, 8, P16, NULL) == ERR_SHAPE
     assert L.fp8mla_probe_read(P16, 1000, 256, 8, P16, NULL) == ERR_SHAPE   # not a multiple of 16
     assert L.fp8mla_probe_read(P16, 1024, 0, 8, P16, NULL) == ERR_SHAPE

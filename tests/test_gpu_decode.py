@@ -111,6 +111,28 @@ def test_high_head_counts_half_tile_edges(dev):
     print("H=%d requests=%d tokens=%d" % (H, len(lengths), sum(lengths)), e)
 
 
+@pytest.mark.parametrize("kind", ["16-head", "64-head"])
+def test_split_count_invariance(dev, kind):
+    """The result does not depend on the split-K partition beyond rounding:
+    the same call cut into at most 1 (no merge), 2 and 7 segments and into
+    the library's own count each matches the oracle, and a bound above the
+    library's own count changes nothing."""
+    if kind == "16-head":
+        w = workloads.small(5, 16, [3000, 50, 9000, 1, 700], seed=5, device=dev, scale=1.3)
+    else:
+        need = _h64_tokens(128)
+        w = workloads.small(3, 128, [need // 2 + 300, 90, need // 2 + 77], seed=6, device=dev)
+    ref = oracle.mla_decode_ref(*oracle_args(w))
+    outs = {}
+    for S in (1, 2, 7, None, 10 ** 6):
+        out = fm.mla_decode_fp8(w.q, w.pool, w.indptr, w.indices, w.scale, w.sm_scale, segments=S)
+        torch.cuda.synchronize()
+        e = assert_attention_close(out, ref, "%s segments=%s" % (kind, S))
+        print(kind, "segments", S, e)
+        outs[S] = out
+    assert torch.equal(outs[None], outs[10 ** 6])
+
+
 def test_all_requests_empty(dev):
     w = workloads.small(4, 16, [0, 0, 0, 0], num_slots=64, device=dev)
     out = _run(w)
