@@ -77,6 +77,48 @@ def _link(objs, path, verbose: bool) -> str:
     return path
 
 
+# A third library, built on request only (``build_sanitized``): the C ABI's
+# host code under AddressSanitizer and UndefinedBehaviorSanitizer, every
+# finding fatal, linked with the release build's other objects.  Each flag
+# applies to the host pass only (device code cannot be sanitized here).  The
+# runtime is not linked into a shared library: a process loading it must
+# preload SANITIZER_RUNTIME.
+SANITIZED_LIB_PATH = os.path.join(BUILD_DIR, "libfp8mla_sanitized.so")
+SANITIZE_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                  "-Xarch_host -fno-sanitize-recover=all "
+                  "-Xarch_host -fno-omit-frame-pointer").split()
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (it carries the
+    UndefinedBehaviorSanitizer handlers too), or '' if none is installed."""
+    cc = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin",
+                      "clang")
+    for c in (cc, "/opt/rocm/llvm/bin/clang", shutil.which("clang") or ""):
+        if c and os.path.exists(c):
+            res = subprocess.run([c, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                                 capture_output=True, text=True)
+            path = res.stdout.strip()
+            if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+            rt = subprocess.run([c, "-print-resource-dir"], capture_output=True, text=True)
+            path = os.path.join(rt.stdout.strip(), "lib", "linux", "libclang_rt.asan-x86_64.so")
+            if rt.returncode == 0 and os.path.exists(path):
+                return path
+    return ""
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Build the release objects and a sanitized C-ABI object, link
+    SANITIZED_LIB_PATH and return it."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = [(s, os.path.basename(s) + ".o", ()) for s in SOURCES[1:]]
+    jobs.append(("api.cpp", "api_sanitized.cpp.o", tuple(SANITIZE_FLAGS)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(j, verbose), jobs))
+    return _link([objs[-1]] + objs[:-1], SANITIZED_LIB_PATH, verbose)
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link both shared libraries; returns the
     release library's path."""
@@ -92,4 +134,7 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv[1:]))
+    if "--sanitized" in sys.argv[1:]:
+        print(build_sanitized(verbose="-v" in sys.argv[1:]))
+    else:
+        print(build(verbose="-v" in sys.argv[1:]))

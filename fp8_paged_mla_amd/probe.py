@@ -9,8 +9,10 @@ from . import _check, _require, _stream_handle, library
 KV_WIDTH = 576
 
 
-def _lib():
-    lib = library()
+def _lib(lib=None):
+    """The library (default the loaded release or debug build) with the probe
+    calls' argument types set."""
+    lib = library() if lib is None else lib
     if not getattr(lib, "_probe_argtypes_set", False):
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         lib.fp8mla_probe_read.argtypes = [vp, i64, i32, i32, vp, vp]
