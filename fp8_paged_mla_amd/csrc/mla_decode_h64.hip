@@ -220,11 +220,29 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       if constexpr (EXT) return head >= p.H || tk >= cc.q_tokens();
       return head >= p.H;
     };
-    pin_q(qr);
-    if (row_idle()) {
+    // Scores enter the softmax as raw * c (c = sm_scale * scale * log2 e)
+    // through one FMA with the exponent's offset, and maxima are taken on the
+    // raw sums: both need c > 0.  A negative c is applied by negating the
+    // query (exact), c = 0 (every score 0) by a zero query and c taken as 1.
+    const float c_in = p.score_scale;
+    const float c_mag = c_in > 0.f ? c_in : (c_in < 0.f ? -c_in : 1.0f);
+    // the landed query of the current request, made ready for the MFMAs
+    auto ready_q = [&]() {
+      pin_q(qr);
+      if (c_in < 0.f) {
 #pragma unroll
-      for (int i = 0; i < QSTEPS; ++i) qr[i] = bf16x8_t{};
-    }
+        for (int i = 0; i < QSTEPS; ++i) {
+          u32x4_t v = __builtin_bit_cast(u32x4_t, qr[i]);
+          v ^= 0x80008000u;
+          qr[i] = __builtin_bit_cast(bf16x8_t, v);
+        }
+      }
+      if (row_idle() || c_in == 0.f) {
+#pragma unroll
+        for (int i = 0; i < QSTEPS; ++i) qr[i] = bf16x8_t{};
+      }
+    };
+    ready_q();
     __syncthreads();  // rows of tile 0 published (by the value waves)
 
     auto record_pieces = [&]() {
@@ -253,11 +271,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
         const int half = h & 1;
         if (q_wait) {
           wait_done(q_op);
-          pin_q(qr);
-          if (row_idle()) {
-#pragma unroll
-            for (int i = 0; i < QSTEPS; ++i) qr[i] = bf16x8_t{};
-          }
+          ready_q();
           q_wait = false;
         }
         const int tile_lo = cc.tile_lo();
@@ -280,14 +294,16 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
           a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv0[2], kv0[3]), qr[2 * i + 1], a0, 0, 0, 0);
           c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16x8(kv1[2], kv1[3]), qr[2 * i + 1], c0, 0, 0, 0);
         }
+        // raw score sums (unscaled); tokens past the end of the request or
+        // the causal limit -inf
         float s0[4], s1[4];
         const int hb = tile_lo + 32 * half;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          s0[r] = a0[r] * p.score_scale;
-          s1[r] = c0[r] * p.score_scale;
+          s0[r] = a0[r];
+          s1[r] = c0[r];
         }
-        if (hb + 32 > tile_hi) {  // (wave-uniform) tokens past the end of the request or limit
+        if (hb + 32 > tile_hi) {  // (wave-uniform)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             s0[r] = hb + s_tok0 + r < tile_hi ? s0[r] : -INFINITY;
@@ -296,8 +312,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
         }
         float lmax = max3f(max3f(s0[0], s0[1], s0[2]), max3f(s0[3], s1[0], s1[1]),
                            max3f(s1[2], s1[3], -INFINITY));
-        lmax = wave_max_over_groups(lmax);  // over the half-tile's 32 tokens
-        const float m_new = fmaxf(m_run, lmax);
+        lmax = wave_max_over_groups(lmax) * c_mag;  // over the half-tile's 32 tokens, scaled
+        const float m_new = max_f32(m_run, lmax);
         // extend: while a token has seen nothing (m -inf), subtract 0 instead
         const float m_sub = EXT && m_new == -INFINITY ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
@@ -307,8 +323,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
         const float m_p = m_sub - kPScaleLog2;  // probabilities scaled by 2^15 (FP16 P.V)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          pr0[r] = __builtin_amdgcn_exp2f(s0[r] - m_p);
-          pr1[r] = __builtin_amdgcn_exp2f(s1[r] - m_p);
+          pr0[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c_mag, -m_p));
+          pr1[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c_mag, -m_p));
         }
         const uint32_t p01 = pack_f16x2(pr0[0], pr0[1]), p23 = pack_f16x2(pr0[2], pr0[3]);
         const uint32_t q01 = pack_f16x2(pr1[0], pr1[1]), q23 = pack_f16x2(pr1[2], pr1[3]);

@@ -133,6 +133,20 @@ def test_split_count_invariance(dev, kind):
     assert torch.equal(outs[None], outs[10 ** 6])
 
 
+@pytest.mark.parametrize("sm_scale", [-0.07, 0.0, 1e-30])
+@pytest.mark.parametrize("H", [16, 128])
+def test_sm_scale_sign_and_zero(dev, H, sm_scale):
+    """The ABI accepts any finite sm_scale.  A negative one flips every
+    score, zero makes the attention a plain mean of the visible values, a
+    tiny one nearly so; the 64-head kernel takes its maxima on unscaled sums
+    and handles a non-positive scale through the query (negated or zeroed)."""
+    n = _h64_tokens(H) if H >= 64 else 3000
+    w = workloads.small(3, H, [n // 2 + 17, 40, n // 2 + 3], seed=41, device=dev,
+                        sm_scale=sm_scale)
+    e = _check_full(w, "H=%d sm_scale=%g" % (H, sm_scale))
+    print("H=%d sm_scale=%g" % (H, sm_scale), e)
+
+
 def test_all_requests_empty(dev):
     w = workloads.small(4, 16, [0, 0, 0, 0], num_slots=64, device=dev)
     out = _run(w)

@@ -50,6 +50,16 @@ def test_head_counts(dev, H, causal):
     _check(w, dev, "H=%d causal=%s" % (H, causal))
 
 
+@pytest.mark.parametrize("sm_scale", [-0.07, 0.0])
+@pytest.mark.parametrize("H", [16, 64])
+def test_sm_scale_sign_and_zero(dev, H, sm_scale):
+    """Any finite sm_scale: negative flips the scores, zero gives the mean of
+    each token's visible values (the kernel negates or zeroes the query)."""
+    w = workloads.extend(3, H, [5, 1, 9], [40, 200, 3], seed=H + 3, causal=True,
+                         sm_scale=sm_scale, scale=1.2)
+    _check(w, dev, "H=%d sm_scale=%g" % (H, sm_scale))
+
+
 @pytest.mark.parametrize("q_lens,history", [
     ([1], [0]),                          # one token, no history
     ([2, 3, 4, 5], [0, 1, 63, 64]),      # ragged blocks around the 4-token block size
