@@ -22,6 +22,7 @@ the roofline of the decode kernels against MI355X's 8 TB/s HBM peak, and the
 CPU oracle timed on the host on a bounded sample.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -348,15 +349,46 @@ def cast_path_step(fm, workloads, torch, dev, args):
                        dtype=torch.uint8, device=dev)
     seq = torch.arange(w0.total_tokens, dtype=torch.int32, device=dev)
 
+    # Every call of every path is checked and marshalled once, so that a
+    # layer's host time (~6 us through the prepared path, ~15 us through the
+    # plain binding) stays below its GPU time and the step is timed on the
+    # GPU, not on the host.  Each call still goes through the C ABI's checks.
+    lib = fm.library()
+    c = ctypes
+    h = c.c_void_p(stream.cuda_stream)
+    N, T = 495552, w0.total_tokens
+
+    def prep(fn, where, *args):
+        return fm.PreparedCall(fn, args, None, None, where)
+
+    cast_calls = [prep(lib.cast_pool_fp8_bf16, "cast_pool_fp8_bf16", c.c_void_p(p.data_ptr()),
+                       c.c_int64(N), c.c_void_p(cast_out.data_ptr()), h) for p in pools]
+    gather_calls = [prep(lib.gather_cast_fp8_bf16, "gather_cast_fp8_bf16",
+                         c.c_void_p(p.data_ptr()), c.c_int64(N), c.c_void_p(w0.indices.data_ptr()),
+                         c.c_int64(T), c.c_void_p(g_out.data_ptr()), h) for p in pools]
+
+    def bf16_call(kv, rows, indices):
+        return prep(lib.mla_decode_bf16, "mla_decode_bf16", c.c_void_p(w0.q.data_ptr()),
+                    c.c_void_p(kv.data_ptr()), c.c_int64(rows), c.c_void_p(w0.indptr.data_ptr()),
+                    c.c_void_p(indices.data_ptr()), c.c_int64(T), c.c_int32(w0.B),
+                    c.c_int32(w0.H), c.c_float(w0.scale), c.c_float(w0.sm_scale),
+                    c.c_void_p(out.data_ptr()), c.c_void_p(ws16.data_ptr()),
+                    c.c_size_t(ws16.numel()), h)
+
+    attend_cast = bf16_call(cast_out, N, w0.indices)
+    attend_gather = bf16_call(g_out, T, seq)
+    fused_calls = [fm.prepare_mla_decode_fp8(w0.q, p, w0.indptr, w0.indices, w0.scale,
+                                             w0.sm_scale, out=out, workspace=ws, stream=stream)
+                   for p in pools]
+    layer_of = {id(p): l for l, p in enumerate(pools)}
+
     def cast_path(p):
-        fm.cast_pool_fp8_bf16(p, out=cast_out)
-        fm.mla_decode_bf16(w0.q, cast_out, w0.indptr, w0.indices, w0.scale, w0.sm_scale,
-                           out=out, workspace=ws16)
+        cast_calls[layer_of[id(p)]]()
+        attend_cast()
 
     def gather_path(p):
-        fm.gather_cast_fp8_bf16(p, w0.indices, out=g_out)
-        fm.mla_decode_bf16(w0.q, g_out, w0.indptr, seq, w0.scale, w0.sm_scale, out=out,
-                           workspace=ws16)
+        gather_calls[layer_of[id(p)]]()
+        attend_gather()
 
     def timed(fn, reps=3):
         best = None
@@ -373,11 +405,10 @@ def cast_path_step(fm, workloads, torch, dev, args):
         return best
 
     for l in range(L):  # warm-up pass
-        fm.cast_pool_fp8_bf16(pools[l], out=cast_out)
-    cast_ms = timed(lambda p: fm.cast_pool_fp8_bf16(p, out=cast_out))
-    gather_ms = timed(lambda p: fm.gather_cast_fp8_bf16(p, w0.indices, out=g_out))
-    fused_ms = timed(lambda p: fm.mla_decode_fp8(w0.q, p, w0.indptr, w0.indices, w0.scale,
-                                                 w0.sm_scale, out=out, workspace=ws))
+        cast_calls[l]()
+    cast_ms = timed(lambda p: cast_calls[layer_of[id(p)]]())
+    gather_ms = timed(lambda p: gather_calls[layer_of[id(p)]]())
+    fused_ms = timed(lambda p: fused_calls[layer_of[id(p)]]())
     cast_path_ms = timed(cast_path)
     gather_path_ms = timed(gather_path)
     cast_bytes = 495552 * 576 * 3
