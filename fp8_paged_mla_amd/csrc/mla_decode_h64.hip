@@ -11,19 +11,19 @@
 //    over the whole tile: S^T = K q^T (MFMA 16x16x32 bf16, K converted from
 //    FP8 in registers, the group's query held in registers), their own online
 //    softmax (every token of the tile belongs to the wave, so no maximum is
-//    exchanged), and FP16 probabilities written to LDS.  Waves 4-7 ("value
-//    waves") each own 128 output columns of all 64 heads: O^T = V^T P^T
+//    exchanged), and FP16 probabilities written to LDS.  Waves 4-11 ("value
+//    waves") each own 64 output columns of all 64 heads: O^T = V^T P^T
 //    (MFMA 16x16x32 f16), each value byte read transposed
 //    (ds_read_b64_tr_b8) and converted once for the four head groups.  A
 //    score wave never holds output accumulators and a value wave never holds
-//    a query, which keeps both within 256 registers at two waves per SIMD,
-//    one of each role, so that one's matrix work can run under the other's
-//    conversions.
+//    a query, which keeps both within 168 registers at three waves per SIMD,
+//    one score and two value waves, so that one's matrix work and another's
+//    conversions can run while the third waits.
 //  * Half-tile pipeline.  Time is cut into half-tile intervals (32 tokens)
 //    separated by one workgroup barrier: in interval h the score waves
 //    produce the probabilities of half-tile h while the value waves consume
 //    those of half-tile h - 1.  The value waves, which have the lighter
-//    share of the arithmetic, also copy the rows global -> LDS (16 rows
+//    share of the arithmetic, also copy the rows global -> LDS (8 rows
 //    each) into three slots of 64 rows, one and a half tiles ahead of use;
 //    the slot ids go through a small LDS ring two tiles ahead of that, so
 //    that no register is ever the destination of a row or id load in flight.
@@ -47,8 +47,8 @@ namespace {
 
 using namespace decode;
 
-constexpr int NWAVES = 8;
-constexpr int THREADS = 64 * NWAVES;              // 512
+constexpr int NWAVES = 12;
+constexpr int THREADS = 64 * NWAVES;              // 768
 constexpr int GROUPS = 4;                         // head groups of 16: one per score wave
 constexpr int WG_HEADS = GROUPS * HEADS;          // 64
 constexpr int TILE = 64;                          // tokens per tile
@@ -59,11 +59,11 @@ constexpr int ROWB = 16 * ROW_SLOTS;              // 592
 constexpr int TILE_BYTES = TILE * ROWB;           // 37888
 constexpr int KSTEPS = KV_WIDTH / 64;             // 9
 constexpr int QSTEPS = 2 * KSTEPS;                // 18
-constexpr int COPIERS = 4;                        // the value waves copy the rows
-constexpr int ROWS_PER_COPIER = TILE / COPIERS;   // 16 rows copied by each value wave
-constexpr int DMA_OPS = (ROWS_PER_COPIER * ROW_SLOTS + 63) / 64;  // 10
-constexpr int VCOLS = V_WIDTH / GROUPS;           // 128 output columns per value wave
-constexpr int VBLOCKS = VCOLS / 16;               // 8 column blocks of 16
+constexpr int COPIERS = 8;                        // the value waves (which also copy the rows)
+constexpr int ROWS_PER_COPIER = TILE / COPIERS;   // 8 rows copied by each value wave
+constexpr int DMA_OPS = (ROWS_PER_COPIER * ROW_SLOTS + 63) / 64;  // 5
+constexpr int VCOLS = V_WIDTH / COPIERS;          // 64 output columns per value wave
+constexpr int VBLOCKS = VCOLS / 16;               // 4 column blocks of 16
 constexpr int ID_SLOTS = 4;                       // slot-id ring entries per copying wave
 static_assert(TILE == 1 << TILE_SHIFT, "tile size");
 static_assert(TILE == kH64TileTokens, "host and kernel tile sizes agree");
@@ -119,11 +119,11 @@ __device__ __forceinline__ void issue_lds_dma4(const void* g, uint32_t lds_base)
 // smaller count only waits longer).  n < 0 cannot occur.
 __device__ __forceinline__ void wait_vm_atmost(int n) {
   n = __builtin_amdgcn_readfirstlane(n);
-  if (n >= 31) wait_vm<31>();
-  else if (n >= 21) wait_vm<21>();
-  else if (n >= 12) wait_vm<12>();
+  if (n >= 16) wait_vm<16>();
   else if (n >= 11) wait_vm<11>();
-  else if (n >= 10) wait_vm<10>();
+  else if (n >= 7) wait_vm<7>();
+  else if (n >= 6) wait_vm<6>();
+  else if (n >= 5) wait_vm<5>();
   else if (n >= 2) wait_vm<2>();
   else if (n >= 1) wait_vm<1>();
   else wait_vm<0>();
@@ -366,15 +366,15 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       __syncthreads();
     }
   } else {
-    // ======================= value wave: columns 128v .. +127 =================
+    // ======================= value wave: columns 64v .. +63 ====================
     const int v = w - GROUPS;
     Cursor lc = cc;  // next tile whose slot ids are copied
     const uint32_t lds_tiles = (uint32_t)(uintptr_t)(
         (__attribute__((address_space(3))) uint8_t*)&kv_lds[0]);
     const uint32_t lds_ids = (uint32_t)(uintptr_t)(
         (__attribute__((address_space(3))) int32_t*)&idring[v][0][0]);
-    // slot ids of the load cursor's tile j: lane r < 16 copies the id of row
-    // 16v + r into ring entry j % 4 (tokens past the request: the tile's
+    // slot ids of the load cursor's tile j: lane r < 8 copies the id of row
+    // 8v + r into ring entry j % 4 (tokens past the request: the tile's
     // first row; past the segment's last tile: entry 0 of kv_indices, unused)
     auto copy_ids = [&](int j) -> int {
       const int ln = opaque_lane();
@@ -387,8 +387,8 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       lc.advance(p, lane);
       return count_ops(1);
     };
-    // rows 16v .. 16v+15 of tile j into slot j % 3: op i fills 16-byte LDS
-    // chunks 64i .. 64i+63 of the wave's block of 16 x 37 (row P / 37, chunk
+    // rows 8v .. 8v+7 of tile j into slot j % 3: op i fills 16-byte LDS
+    // chunks 64i .. 64i+63 of the wave's block of 8 x 37 (row P / 37, chunk
     // P % 37; the pad chunk gets a copy of chunk 35; lanes past the block
     // masked off).  What a lane copies depends on the tile only through the
     // row's slot id, so the rest is computed once: per op, the byte offset
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       for (int c = 0; c < VBLOCKS; ++c) O[hg][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto finish_request = [&](bool complete) {
-      // lane (t, g) holds columns 128v + 16c + 4g + 0..3 of head t of every group
+      // lane (t, g) holds columns 64v + 16c + 4g + 0..3 of head t of every group
       const int ln = opaque_lane();
       const int tt = ln & 15, gg = ln >> 4;
 #pragma unroll

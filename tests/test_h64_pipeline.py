@@ -4,7 +4,7 @@
 The kernel's time is cut into half-tile intervals, each ended by one
 workgroup barrier.  Score waves compute the scores of half-tile h in interval
 h, value waves the P.V of half-tile h - 1.  The value waves also copy the
-rows of each tile (global -> LDS, a quarter each) into slot tile % 3 and the
+rows of each tile (global -> LDS, an eighth each) into slot tile % 3 and the
 slot ids of each tile into their own LDS ring entry tile % 4; score waves
 only load a query per request.  A wave waits with "at most N of my loads
 outstanding"; loads retire in issue order, so such a wait proves every load
@@ -29,7 +29,7 @@ import re
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "fp8_paged_mla_amd", "csrc", "mla_decode_h64.hip")
 
-DMA_OPS = 10       # row-copy ops per value wave per tile (16 rows x 37 chunks of 16 B)
+DMA_OPS = 5        # row-copy ops per value wave per tile (8 rows x 37 chunks of 16 B)
 QSTEPS = 18        # query loads per request (score waves)
 NSLOTS = 3
 ID_SLOTS = 4
@@ -184,8 +184,9 @@ def test_source_matches_model():
     src = open(SRC).read()
     assert "constexpr int NSLOTS = 3;" in src
     assert "constexpr int ID_SLOTS = 4;" in src
-    assert "constexpr int DMA_OPS = (ROWS_PER_COPIER * ROW_SLOTS + 63) / 64;  // 10" in src
-    assert "constexpr int ROWS_PER_COPIER = TILE / COPIERS;   // 16" in src
+    assert "constexpr int DMA_OPS = (ROWS_PER_COPIER * ROW_SLOTS + 63) / 64;  // 5" in src
+    assert "constexpr int ROWS_PER_COPIER = TILE / COPIERS;   // 8" in src
+    assert "constexpr int COPIERS = 8;" in src
     assert "constexpr int QSTEPS = 2 * KSTEPS;                // 18" in src
     for expr in ("if (m + 2 < ntiles) {\n        wait_done(id_a);  // ids of tile m + 2\n        r_new = copy_rows(m + 2);",
                  "id_new = copy_ids(m + 4);\n    };",
