@@ -121,13 +121,16 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
     return l;
   };
   // index of the load cursor's tile, then advance it (past the segment's
-  // last tile the load reads entry 0 and is never used)
+  // last tile the load reads entry 0 and is never used, and the cursor stays
+  // on the last tile rather than walk the rest of the request list)
+  int lc_tile = 0;
   auto load_next_index = [&]() -> int32_t {
     const int tlo = lc.tile_lo();
     const int tok = tlo + 16 * w + t;
-    const int32_t* a = lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) : p.indices;
+    const int32_t* a =
+        lc_tile < ntiles && lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) : p.indices;
     const int32_t v = issue_load_i32(a);
-    lc.advance(p, lane);
+    if (++lc_tile < ntiles) lc.advance(p, lane);
     return v;
   };
   const uint32_t lds_tiles = (uint32_t)(uintptr_t)(
@@ -408,7 +411,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_kernel(const SplitParams p)
       cc = nc;
       whole_request = true;
       record_pieces();
-    } else {
+    } else if (k + 1 < ntiles) {  // (past the last tile the cursor is not needed)
       cc.advance(p, lane);
     }
   };

@@ -358,7 +358,9 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
             issue_load_q(qr, q_ptr(cc));  // waited for at the start of the next interval
             q_op = count_ops(QSTEPS);
             q_wait = true;
-          } else {
+          } else if (m + 1 < ntiles) {
+            // (not past the segment's last tile: the cursor would walk the
+            // rest of the request list, empty padding included, for nothing)
             cc.advance(p, lane);
           }
         }
@@ -375,16 +377,19 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
         (__attribute__((address_space(3))) int32_t*)&idring[v][0][0]);
     // slot ids of the load cursor's tile j: lane r < 8 copies the id of row
     // 8v + r into ring entry j % 4 (tokens past the request: the tile's
-    // first row; past the segment's last tile: entry 0 of kv_indices, unused)
+    // first row; past the segment's last tile: entry 0 of kv_indices, unused,
+    // and the cursor stays on the last tile rather than walk the rest of the
+    // request list)
     auto copy_ids = [&](int j) -> int {
       const int ln = opaque_lane();
       const uint32_t base =
           __builtin_amdgcn_readfirstlane(lds_ids + 4 * ROWS_PER_COPIER * (j & (ID_SLOTS - 1)));
       const int tlo = lc.tile_lo();
       const int tok = tlo + ROWS_PER_COPIER * v + ln;
-      const int32_t* a = lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) : p.indices;
+      const int32_t* a =
+          j < ntiles && lc.nt > 0 ? p.indices + (tok < lc.tile_hi() ? tok : tlo) : p.indices;
       if (ln < ROWS_PER_COPIER) issue_lds_dma4(a, base);
-      lc.advance(p, lane);
+      if (j + 1 < ntiles) lc.advance(p, lane);
       return count_ops(1);
     };
     // rows 8v .. 8v+7 of tile j into slot j % 3: op i fills 16-byte LDS
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
           const bool last_of_request = cc.j + 1 == cc.nt;
           if (last_of_request || pm + 1 == ntiles) finish_request(whole_request && last_of_request);
           if (last_of_request && pm + 1 < ntiles) whole_request = true;
-          cc.advance(p, lane);
+          if (pm + 1 < ntiles) cc.advance(p, lane);
         }
       }
       if (h & 1) wait_copies();

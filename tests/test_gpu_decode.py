@@ -147,6 +147,18 @@ def test_sm_scale_sign_and_zero(dev, H, sm_scale):
     print("H=%d sm_scale=%g" % (H, sm_scale), e)
 
 
+@pytest.mark.parametrize("H", [16, 128])
+def test_trailing_empty_requests(dev, H):
+    """Long requests followed by 150 empty ones (more than a 64-entry window
+    of the request list past the last tile): the tile cursors stop at the
+    segment's last tile instead of walking the empty tail."""
+    n = _h64_tokens(H) if H >= 64 else 5000
+    lengths = [n // 2 + 11, 70, n // 2 + 5] + [0] * 150
+    w = workloads.small(len(lengths), H, lengths, seed=57, device=dev)
+    e = _check_full(w, "H=%d trailing empty" % H)
+    print("H=%d trailing empty requests" % H, e)
+
+
 def test_all_requests_empty(dev):
     w = workloads.small(4, 16, [0, 0, 0, 0], num_slots=64, device=dev)
     out = _run(w)
