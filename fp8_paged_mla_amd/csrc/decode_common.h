@@ -84,6 +84,26 @@ __device__ __forceinline__ RowPair swap_rows16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(u, v, false, false);
   return {__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
 }
+// Output rows from P.V accumulators in the MFMA's O^T layout, where lane
+// (t, g) holds columns 16c + 4g .. 16c + 4g + 3 of row t for each 16-column
+// block c.  Stored as they are, that is 8 bytes per lane and 32 contiguous
+// bytes per row and instruction; such stores measured up to 16% slower than
+// 16-byte ones on calls with many requests (the 64-row kernel at 64 heads,
+// requests of 128 to 4,096 tokens).  Lanes g and g ^ 1 therefore trade a
+// block: pair_blocks takes the packed columns of blocks 2k (a) and 2k + 1 (b)
+// and returns the 8 consecutive columns that start at 32k + paired_col(g),
+// lane g even keeping its block-2k half and taking its partner's, lane g odd
+// the same for block 2k + 1.  A store then writes 16 bytes per lane and 64
+// contiguous bytes per row.  Every lane of the wave must take part.
+__device__ __forceinline__ uint4 pair_blocks(uint2 a, uint2 b) {
+  // v_permlane16_swap: the odd 16-lane rows of the first operand trade with
+  // the even rows of the second
+  const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+  const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+  return make_uint4((uint32_t)x[0], (uint32_t)y[0], (uint32_t)x[1], (uint32_t)y[1]);
+}
+__device__ __forceinline__ int paired_col(int g) { return 4 * g + 12 * (g & 1); }
+
 // max without the canonicalising fmaxf adds to each operand the compiler
 // cannot trace to arithmetic (values loaded, exchanged or merged from two
 // paths): one instruction instead of up to three.  IEEE maxNum otherwise: a

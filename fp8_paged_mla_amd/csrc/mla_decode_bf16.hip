@@ -164,24 +164,34 @@ __global__ __launch_bounds__(THREADS) void mla_split_bf16_kernel(const SplitPara
     float l = 0.f;
 #pragma unroll
     for (int v = 0; v < NWAVES; ++v) l += l_lds[v][t];
-    // lane (t, g) holds columns 128w + 16c + 4g + 0..3 of head t
+    // lane (t, g) holds columns 128w + 16c + 4g + 0..3 of head t; lanes g and
+    // g ^ 1 pair them up for 16-byte stores (pair_blocks)
+    const int col = 128 * w + paired_col(g);  // + 32 k for block pair k
     if (complete) {
-      if (head < p.H) {
-        const float inv = p.kv_scale / l;
-        uint16_t* op = p.out + ((int64_t)cc.b * p.H + head) * V_WIDTH + 128 * w + 4 * g;
+      const float inv = p.kv_scale / l;
+      uint4 d[VBLOCKS / 2];
 #pragma unroll
-        for (int c = 0; c < VBLOCKS; ++c)
-          *reinterpret_cast<uint2*>(op + 16 * c) =
-              make_uint2(pack_bf16x2(O[c][0] * inv, O[c][1] * inv), pack_bf16x2(O[c][2] * inv, O[c][3] * inv));
+      for (int k = 0; k < VBLOCKS / 2; ++k)
+        d[k] = pair_blocks(make_uint2(pack_bf16x2(O[2 * k][0] * inv, O[2 * k][1] * inv),
+                                      pack_bf16x2(O[2 * k][2] * inv, O[2 * k][3] * inv)),
+                           make_uint2(pack_bf16x2(O[2 * k + 1][0] * inv, O[2 * k + 1][1] * inv),
+                                      pack_bf16x2(O[2 * k + 1][2] * inv, O[2 * k + 1][3] * inv)));
+      if (head < p.H) {
+        uint16_t* op = p.out + ((int64_t)cc.b * p.H + head) * V_WIDTH + col;
+#pragma unroll
+        for (int k = 0; k < VBLOCKS / 2; ++k) *reinterpret_cast<uint4*>(op + 32 * k) = d[k];
       }
     } else {
       const int64_t piece = (int64_t)piece_slot(seg, cc.b == span.b0) * p.Hp + head;
       const float inv = 1.0f / l;
-      uint16_t* op = p.part_o + piece * V_WIDTH + 128 * w + 4 * g;
+      uint16_t* op = p.part_o + piece * V_WIDTH + col;
 #pragma unroll
-      for (int c = 0; c < VBLOCKS; ++c)
-        *reinterpret_cast<uint2*>(op + 16 * c) =
-            make_uint2(pack_f16x2(O[c][0] * inv, O[c][1] * inv), pack_f16x2(O[c][2] * inv, O[c][3] * inv));
+      for (int k = 0; k < VBLOCKS / 2; ++k)
+        *reinterpret_cast<uint4*>(op + 32 * k) =
+            pair_blocks(make_uint2(pack_f16x2(O[2 * k][0] * inv, O[2 * k][1] * inv),
+                                   pack_f16x2(O[2 * k][2] * inv, O[2 * k][3] * inv)),
+                        make_uint2(pack_f16x2(O[2 * k + 1][0] * inv, O[2 * k + 1][1] * inv),
+                                   pack_f16x2(O[2 * k + 1][2] * inv, O[2 * k + 1][3] * inv)));
       if (w == 0 && g == 0) p.part_lse[piece] = m_run + __builtin_amdgcn_logf(l) - kPScaleLog2;
     }
 #pragma unroll

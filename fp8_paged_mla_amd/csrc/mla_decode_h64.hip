@@ -64,6 +64,7 @@ constexpr int ROWS_PER_COPIER = TILE / COPIERS;   // 8 rows copied by each value
 constexpr int DMA_OPS = (ROWS_PER_COPIER * ROW_SLOTS + 63) / 64;  // 5
 constexpr int VCOLS = V_WIDTH / COPIERS;          // 64 output columns per value wave
 constexpr int VBLOCKS = VCOLS / 16;               // 4 column blocks of 16
+static_assert(VBLOCKS == 4, "output stores take the column blocks in two pairs");
 constexpr int ID_SLOTS = 4;                       // slot-id ring entries per copying wave
 static_assert(TILE == 1 << TILE_SHIFT, "tile size");
 static_assert(TILE == kH64TileTokens, "host and kernel tile sizes agree");
@@ -490,9 +491,11 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
       for (int c = 0; c < VBLOCKS; ++c) O[hg][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto finish_request = [&](bool complete) {
-      // lane (t, g) holds columns 64v + 16c + 4g + 0..3 of head t of every group
+      // lane (t, g) holds columns 64v + 16c + 4g + 0..3 of head t of every
+      // group; lanes g and g ^ 1 pair them up for 16-byte stores (pair_blocks)
       const int ln = opaque_lane();
       const int tt = ln & 15, gg = ln >> 4;
+      const int col = VCOLS * v + paired_col(gg);  // + 32 k for block pair k
 #pragma unroll
       for (int hg = 0; hg < GROUPS; ++hg) {
         const float l = lfin[hg][tt];
@@ -501,28 +504,40 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
         bool idle = head_g >= p.H;
         if constexpr (EXT) idle = idle || tok_g >= cc.q_tokens();
         if (complete) {
+          // extend: a token with no visible token gets a zero row
+          const float inv = EXT && l == 0.f ? 0.f : p.kv_scale / l;
+          uint4 d[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const f32x4_t& a = O[hg][2 * k];
+            const f32x4_t& b = O[hg][2 * k + 1];
+            d[k] = pair_blocks(make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv),
+                                          pack_bf16x2(a[2] * inv, a[3] * inv)),
+                               make_uint2(pack_bf16x2(b[0] * inv, b[1] * inv),
+                                          pack_bf16x2(b[2] * inv, b[3] * inv)));
+          }
           if (!idle) {
             int64_t orow = cc.b;
             if constexpr (EXT) orow = cc.q_row0() + tok_g;
-            // extend: a token with no visible token gets a zero row
-            const float inv = EXT && l == 0.f ? 0.f : p.kv_scale / l;
-            uint16_t* op = p.out + (orow * p.H + head_g) * V_WIDTH + VCOLS * v + 4 * gg;
-#pragma unroll
-            for (int c = 0; c < VBLOCKS; ++c)
-              *reinterpret_cast<uint2*>(op + 16 * c) =
-                  make_uint2(pack_bf16x2(O[hg][c][0] * inv, O[hg][c][1] * inv),
-                             pack_bf16x2(O[hg][c][2] * inv, O[hg][c][3] * inv));
+            uint16_t* op = p.out + (orow * p.H + head_g) * V_WIDTH + col;
+            *reinterpret_cast<uint4*>(op) = d[0];
+            *reinterpret_cast<uint4*>(op + 32) = d[1];
           }
         } else {
           const int64_t piece = (int64_t)piece_slot(seg, cc.b == span.b0) * p.Hp + row_g;
           const bool empty = EXT && l == 0.f;  // extend: no visible token in this piece
           const float inv = empty ? 0.f : 1.0f / l;
-          uint16_t* op = p.part_o + piece * V_WIDTH + VCOLS * v + 4 * gg;
+          uint16_t* op = p.part_o + piece * V_WIDTH + col;
 #pragma unroll
-          for (int c = 0; c < VBLOCKS; ++c)
-            *reinterpret_cast<uint2*>(op + 16 * c) =
-                make_uint2(pack_f16x2(O[hg][c][0] * inv, O[hg][c][1] * inv),
-                           pack_f16x2(O[hg][c][2] * inv, O[hg][c][3] * inv));
+          for (int k = 0; k < 2; ++k) {
+            const f32x4_t& a = O[hg][2 * k];
+            const f32x4_t& b = O[hg][2 * k + 1];
+            *reinterpret_cast<uint4*>(op + 32 * k) =
+                pair_blocks(make_uint2(pack_f16x2(a[0] * inv, a[1] * inv),
+                                       pack_f16x2(a[2] * inv, a[3] * inv)),
+                            make_uint2(pack_f16x2(b[0] * inv, b[1] * inv),
+                                       pack_f16x2(b[2] * inv, b[3] * inv)));
+          }
           if (v == hg && gg == 0)
             p.part_lse[piece] = empty ? -INFINITY : mfin[hg][tt] + __builtin_amdgcn_logf(l) - kPScaleLog2;
         }
