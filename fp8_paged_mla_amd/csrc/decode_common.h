@@ -14,6 +14,18 @@ constexpr int HEADS = 16;   // query heads per workgroup (the MFMA N dimension)
 constexpr int TILE_W = 4;   // segment balancing: weight of a tile
 constexpr int START_W = 2;  // extra weight of a request's first tile
 
+// Extend calls small enough for the split kernel to lay out its list of
+// virtual requests itself (extend_common.h): the call's own index arrays and
+// where the list goes.  qo_indptr null: the pre-pass kernel built the list.
+struct ExtendList {
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+  int32_t* indptr_out;  // the list's CSR (SplitParams::indptr)
+  int2* vinfo_out;      // SplitParams::vinfo
+  int32_t* hdr;         // {virtual requests, CSR total}, for the combine
+  int32_t batch, total_q, total_kv, T;
+};
+
 struct SplitParams {
   const uint16_t* q;
   const uint8_t* pool;      // KV rows (E4M3FN bytes or BF16 bits)
@@ -43,6 +55,7 @@ struct SplitParams {
   const int2* vinfo;
   int32_t rows_per_tok;  // query rows per token (heads rounded up to 16) if <= 64, else 0
   int32_t causal;
+  ExtendList list;
 };
 
 // P.V runs in FP16 (the FP16 MFMA is as fast as the BF16 one): the E4M3

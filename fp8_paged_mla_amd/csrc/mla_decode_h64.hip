@@ -36,11 +36,13 @@
 //
 // The extend instantiation (EXT) serves several query tokens per request: a
 // workgroup's 64 rows are (token, head) pairs of one virtual request (a
-// request and a block of its query tokens, built on the device), a score
+// request and a block of its query tokens, built on the device: by a pre-pass
+// kernel, or for small calls by wave 0 of every workgroup here), a score
 // wave's 16 rows belong to one token whose causal limit masks its scores,
 // and a token without visible tokens in a piece yields an empty partial
 // (lse -inf).
 #include "decode_host.h"
+#include "extend_common.h"
 
 namespace fp8mla {
 namespace {
@@ -155,6 +157,15 @@ __global__ __launch_bounds__(THREADS) void mla_split_h64_kernel(const SplitParam
   if (item >= p.items) return;
   const int seg = item / p.HG;
   const int hs = item - seg * p.HG;
+
+  if constexpr (EXT) {
+    // a small call's list of virtual requests, laid out here by every
+    // workgroup (same values) instead of by a pre-pass kernel
+    if (p.list.qo_indptr != nullptr) {
+      if (w == 0) build_list_wave(p, lane);
+      __syncthreads();
+    }
+  }
 
   SegmentSpan span;
   // (extend: the virtual requests' CSR counts tiles already)

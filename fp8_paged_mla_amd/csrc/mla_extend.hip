@@ -16,13 +16,15 @@
 //     a block reads the first n tokens of its request's list, n being its
 //     last token's limit; their CSR in 64-token tiles, and per block its
 //     first kv_indices entry, first query row and the tokens of its last
-//     tile.
+//     tile.  Calls of at most 64 requests and 256 list entries skip it: the
+//     split kernel builds the same list itself (extend_common.h).
 //  2. mla_split_h64_kernel<true> runs the 64-row split kernel over them: a
 //     block's T tokens x H heads share every KV tile, each 16-row group
 //     masked by its own token's limit.
 //  3. extend_combine_kernel merges the partials of blocks that span
 //     segments, and writes the zero rows of empty blocks.
 #include "decode_host.h"
+#include "extend_common.h"
 
 namespace fp8mla {
 namespace {
@@ -69,23 +71,6 @@ __device__ __forceinline__ int64_t block_exclusive_scan(int64_t x, int64_t& tota
   return base + inc - x;
 }
 
-__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
-
-// Request b's query rows [q_lo, q_hi) and kv_indices range [kv_lo, kv_hi),
-// each indptr entry clamped into its array so that no access leaves it.
-struct RequestRanges {
-  int q_lo, q_hi, kv_lo, kv_hi;
-};
-__device__ __forceinline__ RequestRanges request_ranges(const int32_t* qo, const int32_t* kv, int b,
-                                                        int total_q, int total_kv) {
-  RequestRanges r;
-  r.q_lo = clampi(qo[b], 0, total_q);
-  r.q_hi = max(r.q_lo, clampi(qo[b + 1], 0, total_q));
-  r.kv_lo = clampi(kv[b], 0, total_kv);
-  r.kv_hi = max(r.kv_lo, clampi(kv[b + 1], 0, total_kv));
-  return r;
-}
-
 // hdr = {virtual requests V, CSR total}; vstart [B + 1]; vindptr [vmax + 1]
 // and vinfo [vmax], entries V.. padded as empty requests, so that the split
 // kernel can walk all vmax of them without reading V.  V is capped at vmax
@@ -98,7 +83,6 @@ __global__ __launch_bounds__(PRE_THREADS) void extend_prepass_kernel(
     int32_t total_q, int32_t total_kv, int32_t T, int32_t causal, int32_t vmax,
     int32_t* __restrict__ hdr, int32_t* __restrict__ vstart, int32_t* __restrict__ vindptr,
     int2* __restrict__ vinfo) {
-  constexpr int TS = kExtendTileShift;
   // blocks per request -> first virtual request of each request
   int64_t carry = 0;
   for (int c = 0; c < B; c += PRE_THREADS) {
@@ -122,8 +106,8 @@ __global__ __launch_bounds__(PRE_THREADS) void extend_prepass_kernel(
   int64_t ncarry = 0;
   for (int c = 0; c < V; c += PRE_THREADS) {
     const int v = c + (int)threadIdx.x;
-    int ntiles = 0, tail = 0;
-    int kv_lo = 0, q_row = 0, ntok = 1;
+    int ntiles = 0;
+    int2 vi = make_int2(0, 0);
     if (v < V) {
       int lo = 0, hi = B - 1;
       while (lo < hi) {
@@ -132,24 +116,15 @@ __global__ __launch_bounds__(PRE_THREADS) void extend_prepass_kernel(
         else hi = mid - 1;
       }
       const RequestRanges r = request_ranges(qo_indptr, kv_indptr, lo, total_q, total_kv);
-      const int ql = r.q_hi - r.q_lo;
-      const int kl = r.kv_hi - r.kv_lo;
-      const int i0 = (v - vstart[lo]) * T;
-      // (the clamps only act on a non-monotone indptr: they keep every query
-      // row the split kernel touches inside [0, total_q))
-      ntok = min(clampi(ql - i0, 1, T), total_q);
-      const int len = causal ? clampi(kl - ql + i0 + ntok, 0, kl) : kl;
-      ntiles = (len >> TS) + ((len & ((1 << TS) - 1)) != 0);
-      tail = len - (ntiles > 0 ? (ntiles - 1) << TS : 0);  // tokens of the last tile, 1 .. 64
-      kv_lo = r.kv_lo;
-      q_row = clampi(r.q_lo + i0, 0, total_q - ntok);
+      const VirtualRequest vr = virtual_request(r, (v - vstart[lo]) * T, T, causal != 0, total_q);
+      ntiles = vr.ntiles;
+      vi = vinfo_of(vr);
     }
     int64_t tot;
     const int64_t pos = ncarry + block_exclusive_scan(ntiles, tot);
     if (v < V) {
       vindptr[v] = (int32_t)min(pos, kExtendMaxTiles);
-      vinfo[v] = make_int2(kv_lo, q_row | ((ntok - 1) << kExtTokShift) |
-                                      ((ntiles > 0 ? tail - 1 : 0) << kExtTailShift));
+      vinfo[v] = vi;
     }
     ncarry += tot;
   }
@@ -281,11 +256,17 @@ hipError_t launch_mla_extend(const uint16_t* q, const uint8_t* kv_pool, int64_t 
   int32_t* vindptr = reinterpret_cast<int32_t*>(ws + pl.vindptr_offset);
   int2* vinfo = reinterpret_cast<int2*>(ws + pl.vinfo_offset);
   int2* pieces = reinterpret_cast<int2*>(ws + pl.pieces_offset);
-  hipLaunchKernelGGL(extend_prepass_kernel, dim3(1), dim3(PRE_THREADS), 0, stream, qo_indptr,
-                     kv_indptr, batch, (int32_t)total_q, (int32_t)total_kv, pl.tokens_per_wg,
-                     causal ? 1 : 0, pl.vmax, hdr, vstart, vindptr, vinfo);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // small calls: the split kernel lays out the list itself (one wave per
+  // workgroup), which saves the pre-pass launch
+  const bool fused_list = batch <= decode::kFusedListMaxBatch && pl.vmax <= decode::kFusedListMaxVirtual;
+  hipError_t e = hipSuccess;
+  if (!fused_list) {
+    hipLaunchKernelGGL(extend_prepass_kernel, dim3(1), dim3(PRE_THREADS), 0, stream, qo_indptr,
+                       kv_indptr, batch, (int32_t)total_q, (int32_t)total_kv, pl.tokens_per_wg,
+                       causal ? 1 : 0, pl.vmax, hdr, vstart, vindptr, vinfo);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   decode::SplitParams sp{};
   sp.q = q;
@@ -310,6 +291,17 @@ hipError_t launch_mla_extend(const uint16_t* q, const uint8_t* kv_pool, int64_t 
   sp.vinfo = vinfo;
   sp.rows_per_tok = pl.rows_per_tok;
   sp.causal = causal ? 1 : 0;
+  if (fused_list) {
+    sp.list.qo_indptr = qo_indptr;
+    sp.list.kv_indptr = kv_indptr;
+    sp.list.indptr_out = vindptr;
+    sp.list.vinfo_out = vinfo;
+    sp.list.hdr = hdr;
+    sp.list.batch = batch;
+    sp.list.total_q = (int32_t)total_q;
+    sp.list.total_kv = (int32_t)total_kv;
+    sp.list.T = pl.tokens_per_wg;
+  }
   e = launch_mla_split_h64_extend(sp, pl.grid, stream);
   if (e != hipSuccess) return e;
 

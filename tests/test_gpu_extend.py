@@ -72,6 +72,22 @@ def test_ragged_blocks(dev, q_lens, history):
     _check(w, dev, "ragged %s/%s" % (q_lens, history))
 
 
+@pytest.mark.parametrize("q_lens", [
+    [12] * 64,               # 64 requests, 256 list entries: the split kernel lays out the list
+    [12] * 63 + [13],        # 257 entries: the pre-pass kernel does
+    [1] * 65,                # 65 requests: the pre-pass kernel does
+    [0, 9, 0, 30, 1, 0, 17, 3] * 8,  # 64 requests, empty ones, 144 list entries in three chunks
+])
+def test_list_in_kernel_and_prepass(dev, q_lens):
+    """Calls of at most 64 requests and 256 virtual requests have their list
+    built inside the split kernel, larger ones by the pre-pass kernel: both
+    sides of both limits against the oracle."""
+    rng = np.random.default_rng(len(q_lens) + sum(q_lens))
+    history = rng.integers(0, 300, size=len(q_lens))
+    w = workloads.extend(len(q_lens), 16, q_lens, history, seed=len(q_lens), causal=True)
+    _check(w, dev, "list B=%d total_q=%d" % (len(q_lens), sum(q_lens)))
+
+
 def test_one_token_per_request_matches_decode(dev):
     w = workloads.extend(6, 16, [1] * 6, [300, 1, 2000, 77, 64, 640], seed=11, scale=0.75)
     got = _run(w, dev)
